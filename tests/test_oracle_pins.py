@@ -1,0 +1,295 @@
+"""Pins for the float64 oracle: each check rests on something other than the
+oracle itself (the pages' worked example, closed forms, invariants of the
+mathematics, pure-Python brute force, or an independent library routine)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _golden():
+    with open(os.path.join(HERE, "golden", "worked_example.json")) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------------------
+# Worked example printed on the page (dgblog.top, "一个简化的计算示例")
+# ---------------------------------------------------------------------------
+def test_worked_example_projection():
+    g = _golden()
+    h = np.array(g["h"], float)[None, :]
+    c_kv, k_r, q_c, q_r = O.project(h, g["W_DKV"], np.zeros((0, 4)), np.zeros((3, 4)),
+                                    n_heads=1, d_head=3, d_rope=0)
+    assert c_kv[0].tolist() == g["expected"]["c_KV"]
+    k, v = O.reconstruct_kv(c_kv, g["W_UK"], g["W_UV"])
+    assert k[0].tolist() == g["expected"]["k"]
+    assert v[0].tolist() == g["expected"]["v"]
+    # cached numbers: k and v per head (2 * n_heads * d_n) against the latent (d_c)
+    assert 2 * g["n_heads"] * g["d_n"] == g["expected"]["cached_numbers_before"]
+    assert c_kv.shape[1] == g["expected"]["cached_numbers_after"]
+
+
+def test_worked_example_single_token_attends_to_its_value():
+    """With one cached token the softmax weight is 1, so out = v exactly."""
+    g = _golden()
+    c_kv = np.array([g["expected"]["c_KV"]], float)
+    w_uk = np.array(g["W_UK"], float)[None]
+    w_uv = np.array(g["W_UV"], float)[None]
+    for q in ([1.0, 1.0, 1.0], [-3.0, 0.5, 7.0]):
+        res = O.explicit_decode(np.array([q]), np.zeros((1, 0)), c_kv, np.zeros((1, 0)),
+                                w_uk, w_uv, scale=1 / math.sqrt(3), base=10000.0)
+        assert res["out"][0].tolist() == g["expected"]["v"]
+        assert res["o_lat"][0].tolist() == g["expected"]["c_KV"]
+
+
+def test_worked_example_absorbed_score():
+    """q . k = (W_UK^T q) . c_KV for the page's matrices: 6 both ways."""
+    g = _golden()
+    q = np.array([1.0, 1.0, 1.0])
+    k = np.array(g["expected"]["k"], float)
+    q_abs = O.absorb_q(q[None, None], np.zeros((1, 1, 0)), np.array(g["W_UK"], float)[None],
+                       np.array([0]), 10000.0)[0, 0]
+    assert q_abs.tolist() == [2.0, 2.0]
+    assert float(q @ k) == 6.0
+    assert float(q_abs @ np.array(g["expected"]["c_KV"], float)) == 6.0
+
+
+# ---------------------------------------------------------------------------
+# Pure-Python brute force (scalar loops, math.fsum) on tiny shapes
+# ---------------------------------------------------------------------------
+def _bf_rope(vec, p, base):
+    d = len(vec)
+    out = []
+    for i in range(d // 2):
+        a = p * base ** (-2.0 * i / d)
+        x, y = vec[2 * i], vec[2 * i + 1]
+        out += [x * math.cos(a) - y * math.sin(a), x * math.sin(a) + y * math.cos(a)]
+    return out
+
+
+def _bf_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale, base):
+    n_h, d_h = len(q_c), len(q_c[0])
+    L, d_c = len(c_kv), len(c_kv[0])
+    outs, lses, olats = [], [], []
+    for h in range(n_h):
+        qr = _bf_rope(q_r[h], L - 1, base)
+        s, vs = [], []
+        for j in range(L):
+            kc = [math.fsum(w_uk[h][i][c] * c_kv[j][c] for c in range(d_c)) for i in range(d_h)]
+            vs.append([math.fsum(w_uv[h][i][c] * c_kv[j][c] for c in range(d_c)) for i in range(d_h)])
+            kr = _bf_rope(k_r[j], j, base)
+            s.append((math.fsum(q_c[h][i] * kc[i] for i in range(d_h))
+                      + math.fsum(qr[i] * kr[i] for i in range(len(kr)))) * scale)
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = math.fsum(e)
+        a = [x / z for x in e]
+        outs.append([math.fsum(a[j] * vs[j][i] for j in range(L)) for i in range(d_h)])
+        olats.append([math.fsum(a[j] * c_kv[j][c] for j in range(L)) for c in range(d_c)])
+        lses.append(m + math.log(z))
+    return np.array(outs), np.array(olats), np.array(lses)
+
+
+@pytest.mark.parametrize("n_h,d_h,d_c,d_r,L", [
+    (1, 3, 2, 0, 1), (1, 3, 2, 2, 2), (2, 4, 4, 2, 5), (2, 3, 4, 4, 6), (1, 4, 2, 4, 6),
+])
+def test_brute_force_matches_oracle(n_h, d_h, d_c, d_r, L):
+    rng = np.random.default_rng(100 + 7 * L + d_r)
+    q_c = rng.standard_normal((n_h, d_h))
+    q_r = rng.standard_normal((n_h, d_r))
+    c_kv = rng.standard_normal((L, d_c))
+    k_r = rng.standard_normal((L, d_r))
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    w_uv = rng.standard_normal((n_h, d_h, d_c))
+    scale, base = 1 / math.sqrt(d_h + d_r), 50.0
+    bo, bl, bs = _bf_decode(q_c.tolist(), q_r.tolist(), c_kv.tolist(), k_r.tolist(),
+                            w_uk.tolist(), w_uv.tolist(), scale, base)
+    ex = O.explicit_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale=scale, base=base, chunk=2)
+    ab = O.absorbed_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale=scale, base=base)
+    for res in (ex, ab):
+        np.testing.assert_allclose(res["out"], bo, rtol=0, atol=1e-13 * np.abs(bo).max())
+        np.testing.assert_allclose(res["o_lat"], bl, rtol=0, atol=1e-13 * np.abs(bl).max())
+        np.testing.assert_allclose(res["lse"], bs, rtol=0, atol=1e-13 * max(1, np.abs(bs).max()))
+
+
+# ---------------------------------------------------------------------------
+# Absorption identity (keybo.xyz, "第二步，推理时的吸收")
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_absorbed_equals_explicit(seed):
+    rng = np.random.default_rng(seed)
+    n_h, d_h, d_c, d_r, L = 3, 8, 16, 8, 37 + seed * 50
+    args = (rng.standard_normal((n_h, d_h)), rng.standard_normal((n_h, d_r)),
+            rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r)),
+            rng.standard_normal((n_h, d_h, d_c)) / 4, rng.standard_normal((n_h, d_h, d_c)) / 4)
+    kw = dict(scale=1 / math.sqrt(d_h + d_r), base=10000.0)
+    ex = O.explicit_decode(*args, **kw, chunk=16)
+    ab = O.absorbed_decode(*args, **kw)
+    for key in ("out", "o_lat", "lse"):
+        ref = ex[key]
+        assert np.abs(ab[key] - ref).max() <= 1e-12 * max(1.0, np.abs(ref).max())
+
+
+def test_absorbed_batch_query_matches_per_sequence():
+    rng = np.random.default_rng(5)
+    B, n_h, d_h, d_c, d_r = 3, 2, 4, 6, 4
+    q_c, q_r = rng.standard_normal((B, n_h, d_h)), rng.standard_normal((B, n_h, d_r))
+    w_uk = rng.standard_normal((n_h, d_h, d_c))
+    pos = np.array([0, 5, 17])
+    q_abs = O.absorb_q(q_c, q_r, w_uk, pos, 10000.0)
+    for b in range(B):
+        for h in range(n_h):
+            np.testing.assert_allclose(q_abs[b, h, :d_c], w_uk[h].T @ q_c[b, h], rtol=1e-14)
+            np.testing.assert_allclose(q_abs[b, h, d_c:], _bf_rope(q_r[b, h].tolist(), pos[b], 10000.0),
+                                       rtol=0, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# RoPE (keybo.xyz, "RoPE 为什么必须解耦")
+# ---------------------------------------------------------------------------
+def test_rope_closed_forms():
+    x = np.array([0.3, -1.7])
+    assert np.array_equal(O.rope(x, 0, 10000.0), x)          # p = 0 is the identity
+    for p in (1.0, 2.5, 1000.0):                                # d = 2: plain rotation by p
+        c, s = math.cos(p), math.sin(p)
+        np.testing.assert_allclose(O.rope(x, p, 10000.0), [0.3 * c + 1.7 * s, 0.3 * s - 1.7 * c],
+                                   rtol=0, atol=1e-15)
+    # d = 4, base 100: frequencies 1 and 100^(-1/2) = 0.1
+    np.testing.assert_allclose(O.rope_inv_freq(4, 100.0), [1.0, 0.1], rtol=1e-15)
+    p = 3.0
+    np.testing.assert_allclose(O.rope(np.array([1.0, 0.0, 1.0, 0.0]), p, 100.0),
+                               [math.cos(p), math.sin(p), math.cos(0.1 * p), math.sin(0.1 * p)],
+                               rtol=0, atol=1e-15)
+
+
+def test_rope_norm_and_relative_position():
+    rng = np.random.default_rng(3)
+    q, k = rng.standard_normal(64), rng.standard_normal(64)
+    for i, j in ((0, 0), (3, 11), (4000, 131071)):
+        np.testing.assert_allclose(np.linalg.norm(O.rope(q, i, 1e4)), np.linalg.norm(q), rtol=1e-14)
+        lhs = O.rope(q, i, 1e4) @ O.rope(k, j, 1e4)
+        # (R_i q)^T (R_j k) = q^T R_(j-i) k
+        assert abs(lhs - q @ O.rope(k, j - i, 1e4)) < 1e-9
+
+
+def test_decode_is_shift_invariant():
+    rng = np.random.default_rng(4)
+    n_h, d_h, d_c, d_r, L = 2, 4, 8, 8, 20
+    args = (rng.standard_normal((n_h, d_h)), rng.standard_normal((n_h, d_r)),
+            rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r)),
+            rng.standard_normal((n_h, d_h, d_c)), rng.standard_normal((n_h, d_h, d_c)))
+    kw = dict(scale=0.3, base=10000.0)
+    a = O.explicit_decode(*args, **kw)
+    for delta in (1, 777, 100000):
+        b = O.explicit_decode(*args, **kw, q_pos=L - 1 + delta, k_pos=np.arange(L) + delta)
+        np.testing.assert_allclose(b["out"], a["out"], rtol=0, atol=1e-9)
+        np.testing.assert_allclose(b["lse"], a["lse"], rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------------------
+# Softmax and weighted sum
+# ---------------------------------------------------------------------------
+def test_softmax_rows_sum_to_one_and_two_token_closed_form():
+    rng = np.random.default_rng(6)
+    n_h, d_h, d_c, d_r = 3, 4, 6, 2
+    w_uk, w_uv = rng.standard_normal((2, n_h, d_h, d_c))
+    q_c, q_r = rng.standard_normal((n_h, d_h)), rng.standard_normal((n_h, d_r))
+    c_kv, k_r = rng.standard_normal((40, d_c)), rng.standard_normal((40, d_r))
+    res = O.explicit_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale=0.5, base=10000.0,
+                            return_weights=True)
+    assert np.abs(res["weights"].sum(axis=1) - 1).max() < 1e-14
+    # two tokens: a_1 = sigmoid(s_1 - s_0)
+    res2 = O.explicit_decode(q_c, q_r, c_kv[:2], k_r[:2], w_uk, w_uv, scale=0.5, base=10000.0,
+                             return_weights=True)
+    for h in range(n_h):
+        qr = O.rope(q_r[h], 1, 10000.0)
+        s = [(q_c[h] @ (w_uk[h] @ c_kv[j]) + qr @ O.rope(k_r[j], j, 10000.0)) * 0.5 for j in (0, 1)]
+        assert abs(res2["weights"][h, 1] - 1 / (1 + math.exp(s[0] - s[1]))) < 1e-14
+
+
+def test_identical_latents_give_projected_value():
+    rng = np.random.default_rng(7)
+    n_h, d_h, d_c, d_r, L = 2, 5, 6, 4, 9
+    c = rng.standard_normal(d_c)
+    w_uk, w_uv = rng.standard_normal((2, n_h, d_h, d_c))
+    res = O.explicit_decode(rng.standard_normal((n_h, d_h)), rng.standard_normal((n_h, d_r)),
+                            np.tile(c, (L, 1)), rng.standard_normal((L, d_r)), w_uk, w_uv,
+                            scale=1.0, base=10000.0)
+    for h in range(n_h):
+        np.testing.assert_allclose(res["out"][h], w_uv[h] @ c, rtol=1e-13)
+
+
+def test_empty_sequence():
+    res = O.explicit_decode(np.ones((2, 3)), np.ones((2, 2)), np.zeros((0, 4)), np.zeros((0, 2)),
+                            np.ones((2, 3, 4)), np.ones((2, 3, 4)), scale=1.0, base=1e4)
+    assert np.all(res["out"] == 0) and np.all(res["o_lat"] == 0) and np.all(res["lse"] == -np.inf)
+    lat = O.latent_decode(np.ones((2, 6)), np.zeros((0, 6)), 4, 1.0)
+    assert np.all(lat["o_lat"] == 0) and np.all(lat["lse"] == -np.inf)
+
+
+# ---------------------------------------------------------------------------
+# Paging (keybo.xyz, "所以 cache 逻辑到底哪里要重写": paged by token latent)
+# ---------------------------------------------------------------------------
+def test_paged_gather_is_exact_under_any_page_table():
+    rng = np.random.default_rng(8)
+    bs, D, L = 4, 6, 13
+    rows = rng.standard_normal((L, D))
+    n_pages = (L + bs - 1) // bs
+    for perm in (np.arange(n_pages), rng.permutation(n_pages + 3)[:n_pages]):
+        pool = np.full((n_pages + 3, bs, D), np.nan)
+        for j in range(L):
+            s = O.slot_of(perm, j, bs)
+            pool[s // bs, s % bs] = rows[j]
+        assert np.array_equal(O.gather_pages(pool, perm, L), rows)
+
+
+# ---------------------------------------------------------------------------
+# Rounding of expected values: against independent implementations
+# ---------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch_and_definition():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.standard_normal(10000) * 10.0 ** rng.integers(-20, 20, 10000),
+                        [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(1.0 + 2.0 ** -8), 0.0, -0.0]])
+    ours = O.to_bf16(x)
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(ours.view(np.uint32), ref.view(np.uint32))
+    # ties to even at 1 + 2^-8 (down to 1) and 1 + 3*2^-8 (up to 1 + 2^-6)
+    assert ours[-5] == 1.0 and ours[-4] == 1.0 + 2.0 ** -6
+
+
+# ---------------------------------------------------------------------------
+# Planted mistakes: a pin above must fail for each
+# ---------------------------------------------------------------------------
+def _mutant_rope_half_split(x, pos, base):
+    x = np.asarray(x, float)
+    d = x.shape[-1]
+    if d == 0:
+        return x.copy()
+    ang = np.asarray(pos, float)[..., None] * O.rope_inv_freq(d, base)
+    c, s = np.cos(ang), np.sin(ang)
+    x0, x1 = x[..., : d // 2], x[..., d // 2:]
+    return np.concatenate([x0 * c - x1 * s, x0 * s + x1 * c], axis=-1)
+
+
+def _mutant_up_project_transposed(c_kv, w_h):
+    w = np.asarray(w_h, float)
+    return np.asarray(c_kv, float) @ w[:, ::-1].T  # wrong column order of W
+
+
+@pytest.mark.parametrize("name,mutant", [("rope", _mutant_rope_half_split),
+                                         ("up_project", _mutant_up_project_transposed)])
+def test_pins_catch_planted_mistakes(monkeypatch, name, mutant):
+    monkeypatch.setattr(O, name, mutant)
+    with pytest.raises(AssertionError):
+        if name == "rope":
+            test_rope_closed_forms()
+            test_brute_force_matches_oracle(2, 3, 4, 4, 6)
+        else:
+            test_worked_example_projection()
