@@ -1,0 +1,112 @@
+// C ABI: argument validation and dispatch.  Every check happens before any
+// HIP call, so an invalid request launches nothing (and these paths run on a
+// machine without a GPU).
+#include <math.h>
+
+#include "mla_internal.h"
+
+namespace {
+
+thread_local int32_t g_last_hip_error = 0;
+
+constexpr int32_t kMaxWidth = 1024;   // d_head, d_latent + d_rope limit of the generic kernels
+
+bool valid_dtype(int32_t t, bool allow_e4m3) {
+  return t == MLA_F32 || t == MLA_BF16 || (allow_e4m3 && t == MLA_E4M3);
+}
+
+mla_status check_dims(const mla_dims* d) {
+  if (!d) return MLA_ERR_NULL;
+  if (d->n_heads < 1 || d->d_head < 1 || d->d_latent < 1 || d->d_rope < 0 || d->block_size < 1)
+    return MLA_ERR_SHAPE;
+  if (d->d_rope % 2 != 0) return MLA_ERR_SHAPE;
+  if (d->d_head > kMaxWidth || d->d_latent + d->d_rope > kMaxWidth || d->block_size > 4096)
+    return MLA_ERR_SHAPE;
+  if (!valid_dtype(d->act_dtype, false) || !valid_dtype(d->kv_dtype, true)) return MLA_ERR_DTYPE;
+  if (!isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+  if (d->d_rope > 0 && !(d->rope_base > 0.0 && isfinite(d->rope_base))) return MLA_ERR_SHAPE;
+  return MLA_OK;
+}
+
+mla_status hip_status(hipError_t e) {
+  if (e == hipSuccess) return MLA_OK;
+  g_last_hip_error = static_cast<int32_t>(e);
+  return MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status mla_absorb_q(const mla_dims* dims, int32_t batch, const void* q_c, const void* q_r,
+                        const int32_t* q_pos, const void* w_uk, void* q_abs, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return MLA_ERR_SHAPE;
+  if (!q_c || !q_pos || !w_uk || !q_abs || (dims->d_rope > 0 && !q_r)) return MLA_ERR_NULL;
+  return hip_status(mla::launch_absorb_q(*dims, batch, q_c, q_r, q_pos, w_uk, q_abs,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_cache_append(const mla_dims* dims, int32_t n_tokens, const void* c_kv,
+                            const void* k_r, const int32_t* pos, const int64_t* slot,
+                            int64_t num_pages, void* kv_cache, float* kv_scale, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!c_kv || !pos || !slot || !kv_cache || (dims->d_rope > 0 && !k_r)) return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  return hip_status(mla::launch_cache_append(*dims, n_tokens, c_kv, k_r, pos, slot, kv_cache,
+                                             kv_scale, static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || num_splits < 0 || num_splits > 65536) return 0;
+  return mla::plan_decode(*dims, batch, num_splits).ws_bytes;
+}
+
+mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_abs, const void* kv_cache,
+                      const float* kv_scale, const int32_t* block_table, int32_t max_pages,
+                      const int32_t* seq_lens, int32_t num_splits, void* workspace,
+                      size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 1 || max_pages < 1 || num_splits < 0 || num_splits > 65536) return MLA_ERR_SHAPE;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !workspace || !o_lat) return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MLA_ERR_WORKSPACE;
+  const mla::DecodePlan plan = mla::plan_decode(*dims, batch, num_splits);
+  if (workspace_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
+  return hip_status(mla::launch_decode(*dims, plan, batch, q_abs, kv_cache, kv_scale, block_table,
+                                       max_pages, seq_lens, workspace, o_lat, lse,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_up_v(const mla_dims* dims, int32_t batch, const void* o_lat, const void* w_uv,
+                    void* out, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 1) return MLA_ERR_SHAPE;
+  if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
+  return hip_status(mla::launch_up_v(*dims, batch, o_lat, w_uv, out, static_cast<hipStream_t>(stream)));
+}
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "required pointer is NULL";
+    case MLA_ERR_SHAPE: return "size out of range or unsupported";
+    case MLA_ERR_DTYPE: return "unknown or unsupported dtype";
+    case MLA_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case MLA_ERR_UNSUPPORTED: return "no kernel for this request";
+    case MLA_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t mla_last_hip_error(void) { return g_last_hip_error; }
+
+int32_t mla_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,127 @@
+// Device helpers shared by the library's kernels (gfx950).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <stdint.h>
+
+namespace mla {
+
+// ---- storage types ---------------------------------------------------------
+struct bf16_t { uint16_t bits; };
+struct e4m3_t { uint8_t bits; };
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+// float32 -> bfloat16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// E4M3 (OCP): exponent bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  uint32_t s = (c >> 7) & 1u, e = (c >> 3) & 0xFu, m = c & 7u;
+  float mag = (e == 0) ? static_cast<float>(m) * 0.001953125f  // m * 2^-9
+                       : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return s ? -mag : mag;
+}
+// float32 -> E4M3 code: nearest, ties to even, saturating at +-448.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float y) {
+  uint32_t u = __float_as_uint(y);
+  uint32_t sign = (u >> 31) << 7;
+  uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {                 // |y| >= 448
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {           // |y| < 2^-6: subnormal grid of step 2^-9
+    float m = __builtin_rintf(__uint_as_float(a) * 512.0f);   // exact scaling, RNE
+    code = static_cast<uint32_t>(m);      // m == 8 is the smallest normal, code 0x08
+  } else {
+    uint32_t q = a >> 20;                 // exponent and top 3 mantissa bits
+    uint32_t rem = a & 0xFFFFFu;
+    q += (rem > 0x80000u) || (rem == 0x80000u && (q & 1u));
+    code = q - (120u << 3);               // rebias 127 -> 7
+    if (code > 0x7Eu) code = 0x7Eu;       // rounding up past 448 saturates
+  }
+  return code | sign;
+}
+
+template <typename T> struct io;
+template <> struct io<float> {
+  __device__ static float load(const float* p, int64_t i) { return p[i]; }
+  __device__ static void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct io<bf16_t> {
+  __device__ static float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i].bits); }
+  __device__ static void store(bf16_t* p, int64_t i, float v) { p[i].bits = f32_to_bf16(v); }
+};
+
+// RoPE of one pair (x0, x1) at position pos, frequency index i of d_rope/2:
+// angle = pos * base^(-2i/d_rope); rotation in float64 without contraction,
+// result rounded to float32.
+__device__ __forceinline__ void rope_pair(float x0, float x1, int32_t pos, int i, int d_rope,
+                                          double base, float* y0, float* y1) {
+#pragma clang fp contract(off)
+  double inv = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(d_rope));
+  double ang = static_cast<double>(pos) * inv;
+  double c = cos(ang), s = sin(ang);
+  double a = static_cast<double>(x0), b = static_cast<double>(x1);
+  double r0 = a * c - b * s;
+  double r1 = a * s + b * c;
+  *y0 = static_cast<float>(r0);
+  *y1 = static_cast<float>(r1);
+}
+
+// ---- split-KV schedule -----------------------------------------------------
+// The batch's pages are flattened in sequence order (sequence b owns
+// ceil(L_b / block_size) consecutive pages) and cut into `parts` contiguous
+// ranges: part w covers [floor(w P / W), floor((w+1) P / W)).  A (part,
+// sequence) overlap is a segment; its partial result lives in slot w + b.
+__device__ __forceinline__ int64_t part_start(int64_t w, int64_t P, int64_t W) { return (w * P) / W; }
+__device__ __forceinline__ int64_t part_of_page(int64_t x, int64_t P, int64_t W) {
+  return ((x + 1) * W - 1) / P;
+}
+__device__ __forceinline__ int32_t pages_of(int32_t L, int32_t bs) { return (L + bs - 1) / bs; }
+
+// Block-wide page prefix over sequences.  `scan` is __shared__ scratch of
+// blockDim.x + 1 ints.  After the call scan[t] = pages of sequences before
+// thread t's chunk [t*chunk, (t+1)*chunk) and scan[blockDim.x] = total P.
+__device__ __forceinline__ void page_prefix(const int32_t* seq_lens, int32_t B, int32_t bs,
+                                            int32_t* scan, int32_t* chunk_out) {
+  const int nt = blockDim.x, t = threadIdx.x;
+  const int32_t chunk = (B + nt - 1) / nt;
+  int32_t s = 0;
+  for (int32_t b = t * chunk; b < min(B, (t + 1) * chunk); ++b) s += pages_of(seq_lens[b], bs);
+  scan[t + 1] = s;
+  if (t == 0) scan[0] = 0;
+  __syncthreads();
+  if (t == 0) {
+    for (int i = 1; i <= nt; ++i) scan[i] += scan[i - 1];
+  }
+  __syncthreads();
+  *chunk_out = chunk;
+}
+// Sequence owning flattened page x (0 <= x < P), and that sequence's first page.
+__device__ __forceinline__ void locate_page(const int32_t* seq_lens, int32_t B, int32_t bs,
+                                            const int32_t* scan, int32_t chunk, int64_t x,
+                                            int32_t* b_out, int64_t* first_out) {
+  int lo = 0, hi = blockDim.x;            // scan[lo] <= x < scan[hi]
+  while (hi - lo > 1) {
+    int mid = (lo + hi) >> 1;
+    if (scan[mid] <= x) lo = mid; else hi = mid;
+  }
+  int64_t first = scan[lo];
+  int32_t b = lo * chunk;
+  for (;;) {
+    int32_t np = pages_of(seq_lens[b], bs);
+    if (x < first + np) break;
+    first += np;
+    ++b;
+  }
+  *b_out = b;
+  *first_out = first;
+}
+
+}  // namespace mla

@@ -1,0 +1,40 @@
+// Internal launcher interface between the C ABI layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "../../include/mla.h"
+
+namespace mla {
+
+// Number of compute units the launch geometry is planned for (MI355X).
+constexpr int kNumCU = 256;
+
+struct DecodePlan {
+  int32_t parts;          // W: KV chunks the flattened page list is cut into
+  int32_t head_groups;    // workgroups per part (heads split across them)
+  bool mfma;              // MFMA kernel (else the generic one)
+  size_t ws_bytes;        // workspace needed
+};
+
+DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits);
+
+hipError_t launch_absorb_q(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
+                           const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t s);
+hipError_t launch_cache_append(const mla_dims& d, int32_t T, const void* c_kv, const void* k_r,
+                               const int32_t* pos, const int64_t* slot, void* cache,
+                               float* kv_scale, hipStream_t s);
+hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
+                         const void* cache, const float* kv_scale, const int32_t* block_table,
+                         int32_t max_pages, const int32_t* seq_lens, void* ws, void* o_lat,
+                         float* lse, hipStream_t s);
+hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
+                       hipStream_t s);
+
+// Whether the MFMA decode kernel handles these dims.
+bool mfma_decode_supported(const mla_dims& d);
+hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
+                              const void* q_abs, const void* cache, const float* kv_scale,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, float* ws_o, float* ws_lse, void* o_lat,
+                              float* lse, hipStream_t s);
+
+}  // namespace mla

@@ -1,0 +1,138 @@
+"""Torch-facing binding: the four calls of include/mla.h with the same names.
+
+Argument marshalling only (dtype/shape/device checks, data pointers, the
+current HIP stream).  Every step of the computation runs in the HIP library;
+there is no CPU or PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+from ._lib import MLA_BF16, MLA_E4M3, MLA_F32, Dims, check
+
+_TORCH = {MLA_F32: torch.float32, MLA_BF16: torch.bfloat16}
+
+
+def make_dims(n_heads: int, d_head: int, d_latent: int, d_rope: int, block_size: int = 64,
+              act: str = "bf16", kv: str = "bf16", softmax_scale: float | None = None,
+              rope_base: float = 10000.0) -> Dims:
+    codes = {"f32": MLA_F32, "bf16": MLA_BF16, "e4m3": MLA_E4M3}
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(d_head + d_rope)
+    return Dims(n_heads, d_head, d_latent, d_rope, block_size, codes[act], codes[kv],
+                softmax_scale, rope_base)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _kv_torch(d: Dims):
+    return (torch.uint8, torch.float8_e4m3fn) if d.kv_dtype == MLA_E4M3 else _TORCH[d.kv_dtype]
+
+
+def absorb_q(d: Dims, q_c, q_r, q_pos, w_uk, q_abs=None, stream=None):
+    """q_abs = [W_UK^T q_C || RoPE(q_R, q_pos)] per batch row and head."""
+    at = _TORCH[d.act_dtype]
+    B = q_c.shape[0]
+    D = d.d_latent + d.d_rope
+    _need(q_c, "q_c", at, (B, d.n_heads, d.d_head))
+    if d.d_rope:
+        _need(q_r, "q_r", at, (B, d.n_heads, d.d_rope))
+    _need(q_pos, "q_pos", torch.int32, (B,))
+    _need(w_uk, "w_uk", at, (d.n_heads, d.d_head, d.d_latent))
+    if q_abs is None:
+        q_abs = torch.empty((B, d.n_heads, D), dtype=at, device=q_c.device)
+    _need(q_abs, "q_abs", at, (B, d.n_heads, D))
+    check(_lib.lib().mla_absorb_q(ctypes.byref(d), B, _ptr(q_c), _ptr(q_r), _ptr(q_pos), _ptr(w_uk),
+                                  _ptr(q_abs), _stream(stream)), "mla_absorb_q")
+    return q_abs
+
+
+def cache_append(d: Dims, c_kv, k_r, pos, slot, kv_cache, kv_scale=None, stream=None):
+    """Write [c_kv || RoPE(k_r, pos)] rows into kv_cache at the given slots."""
+    at = _TORCH[d.act_dtype]
+    T = c_kv.shape[0]
+    D = d.d_latent + d.d_rope
+    _need(c_kv, "c_kv", at, (T, d.d_latent))
+    if d.d_rope:
+        _need(k_r, "k_r", at, (T, d.d_rope))
+    _need(pos, "pos", torch.int32, (T,))
+    _need(slot, "slot", torch.int64, (T,))
+    _need(kv_cache, "kv_cache", _kv_torch(d))
+    if kv_cache.dim() != 3 or kv_cache.shape[1] != d.block_size or kv_cache.shape[2] != D:
+        raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)}")
+    if d.kv_dtype == MLA_E4M3:
+        _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    check(_lib.lib().mla_cache_append(ctypes.byref(d), T, _ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot),
+                                      kv_cache.shape[0], _ptr(kv_cache), _ptr(kv_scale), _stream(stream)),
+          "mla_cache_append")
+
+
+def decode_workspace_bytes(d: Dims, batch: int, num_splits: int = 0) -> int:
+    return int(_lib.lib().mla_decode_workspace_bytes(ctypes.byref(d), batch, num_splits))
+
+
+def decode(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_splits: int = 0,
+           workspace=None, o_lat=None, lse=None, stream=None):
+    """Absorbed attention over the paged latent cache; returns (o_lat, lse)."""
+    at = _TORCH[d.act_dtype]
+    B = q_abs.shape[0]
+    D = d.d_latent + d.d_rope
+    _need(q_abs, "q_abs", at, (B, d.n_heads, D))
+    _need(kv_cache, "kv_cache", _kv_torch(d))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    if d.kv_dtype == MLA_E4M3:
+        _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    need = decode_workspace_bytes(d, B, num_splits)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
+    if o_lat is None:
+        o_lat = torch.empty((B, d.n_heads, d.d_latent), dtype=at, device=q_abs.device)
+    _need(o_lat, "o_lat", at, (B, d.n_heads, d.d_latent))
+    if lse is None:
+        lse = torch.empty((B, d.n_heads), dtype=torch.float32, device=q_abs.device)
+    _need(lse, "lse", torch.float32, (B, d.n_heads))
+    check(_lib.lib().mla_decode(ctypes.byref(d), B, _ptr(q_abs), _ptr(kv_cache), _ptr(kv_scale),
+                                _ptr(block_table), block_table.shape[1], _ptr(seq_lens), num_splits,
+                                _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _ptr(o_lat), _ptr(lse), _stream(stream)), "mla_decode")
+    return o_lat, lse
+
+
+def up_v(d: Dims, o_lat, w_uv, out=None, stream=None):
+    """out = W_UV o_lat per batch row and head."""
+    at = _TORCH[d.act_dtype]
+    B = o_lat.shape[0]
+    _need(o_lat, "o_lat", at, (B, d.n_heads, d.d_latent))
+    _need(w_uv, "w_uv", at, (d.n_heads, d.d_head, d.d_latent))
+    if out is None:
+        out = torch.empty((B, d.n_heads, d.d_head), dtype=at, device=o_lat.device)
+    _need(out, "out", at, (B, d.n_heads, d.d_head))
+    check(_lib.lib().mla_up_v(ctypes.byref(d), B, _ptr(o_lat), _ptr(w_uv), _ptr(out), _stream(stream)),
+          "mla_up_v")
+    return out

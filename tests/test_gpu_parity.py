@@ -1,0 +1,121 @@
+"""GPU parity: every call of the decode chain against the float64 oracle on
+identical seeded inputs, through the C ABI.  Tolerances: max|gpu - ref| <=
+tol * max|ref| with tol = 1e-5 (fp32), 1e-2 (bf16), 3e-2 (e4m3 cache, against
+the oracle on its own dequantised rows); lse uses tol * max(1, |lse|)."""
+import numpy as np
+import pytest
+import torch
+
+import mla_inputs as W
+from oracle import mla_oracle as O
+
+import chain as C
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+def _check_all(w, res, heads=None, seqs=None, tol=None):
+    tol = tol or C.TOL[w.kv if w.kv == "e4m3" else w.act]
+    seqs = range(w.B) if seqs is None else seqs
+    # absorb_q
+    q_ref = O.absorb_q(w.q_c, w.q_r, w.w_uk, w.q_pos, w.rope_base)
+    assert C.rel_err(C.f64(res["q_abs"]), q_ref) <= C.TOL[w.act]
+    for b in seqs:
+        ref = C.oracle_decode(w, b, heads=heads)
+        hs = ref["heads"]
+        assert C.rel_err(C.f64(res["out"][b, hs]), ref["out"]) <= tol, f"out b={b}"
+        assert C.rel_err(C.f64(res["o_lat"][b, hs]), ref["o_lat"]) <= tol, f"o_lat b={b}"
+        assert C.lse_err(C.f64(res["lse"][b, hs]), ref["lse"]) <= tol, f"lse b={b}"
+
+
+def test_tiny_fp32_chain():
+    w = C.tiny_inputs(W.make("tiny_f32"))
+    res = C.run_chain(w)
+    _check_all(w, res)
+    rows = C.gather_rows(w, res, 0)["stored"]
+    assert C.rel_err(rows, C.oracle_rows(w, 0)["stored"]) <= 1e-6
+
+
+@pytest.mark.parametrize("splits", [0, 1, 2, 5])
+def test_tiny_fp32_splits(splits):
+    w = C.tiny_inputs(W.make("tiny_f32"))
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res)
+
+
+def test_bf16_cache_rows_are_rounded_rows():
+    w = W.make("v2_b16_4k", B=3, lens=[1, 130, 257])
+    res = C.run_chain(w)
+    for b in range(w.B):
+        got = C.gather_rows(w, res, b)["stored"]
+        exp = C.oracle_rows(w, b)["stored"]
+        assert np.array_equal(got[:, :w.d_c], exp[:, :w.d_c])           # latent copied exactly
+        ulp = np.abs(got[:, w.d_c:] - exp[:, w.d_c:]) / np.maximum(np.abs(exp[:, w.d_c:]), 1e-30)
+        assert (ulp <= 2.0 ** -8).all()                                  # RoPE part: <= 1 bf16 ulp
+
+
+@pytest.mark.parametrize("lens,splits", [([1, 130, 257], 0), ([64, 65, 63], 3), ([300], 64),
+                                         ([700, 1, 129, 64], 7)])
+def test_bf16_v2_shapes(lens, splits):
+    w = W.make("v2_b16_4k", B=len(lens), lens=lens)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res)
+
+
+def test_empty_sequence_in_batch():
+    w = W.make("v2_b16_4k", B=3, lens=[70, 0, 5])
+    res = C.run_chain(w, num_splits=4)
+    o = C.f64(res["o_lat"][1])
+    assert np.all(o == 0) and np.all(C.f64(res["out"][1]) == 0)
+    assert np.all(np.isneginf(C.f64(res["lse"][1])))
+    _check_all(w, res, seqs=[0, 2])
+
+
+@pytest.mark.parametrize("splits", [1, 2, 8, 32, 64])
+def test_ragged_shuffled_pages_any_split(splits):
+    w = W.make("ragged_b64", B=4, lens=[1000, 65, 333, 1024], n_h=128)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res, heads=[0, 1, 63, 127])
+
+
+def test_page_permutation_is_bitwise_invariant():
+    import copy
+    a = W.make("ragged_b64", B=3, lens=[200, 450, 130], shuffle=False)
+    b = copy.copy(a)
+    perm = np.random.default_rng(11).permutation(a.num_pages).astype(np.int32)
+    b.block_table = np.where(a.block_table >= 0, perm[np.maximum(a.block_table, 0)], -1).astype(np.int32)
+    assert not np.array_equal(a.block_table, b.block_table)
+    ra, rb = C.run_chain(a, num_splits=4), C.run_chain(b, num_splits=4)
+    for k in ("o_lat", "lse", "out"):
+        assert torch.equal(ra[k], rb[k]), k
+
+
+def test_run_to_run_deterministic():
+    w = W.make("ragged_b64", B=2, lens=[900, 77])
+    r1 = C.run_chain(w, num_splits=6)
+    r2 = C.run_chain(w, num_splits=6)
+    for k in ("o_lat", "lse", "out", "q_abs"):
+        assert torch.equal(r1[k], r2[k]), k
+
+
+def test_fp8_cache_bytes_match_oracle_quantiser():
+    w = W.make("fp8_h16_b128", B=3, lens=[513, 64, 1000])
+    res = C.run_chain(w)
+    for b in range(w.B):
+        got, exp = C.gather_rows(w, res, b), C.oracle_rows(w, b)
+        mism = (got["codes"] != exp["codes"])
+        assert mism.mean() <= 1e-6, f"b={b}: {mism.sum()} codes differ"
+        assert np.all(np.abs(got["scales"] - exp["scales"]) <= 2.0 ** -23 * np.abs(exp["scales"]))
+
+
+@pytest.mark.parametrize("lens,splits", [([513, 64, 1000], 0), ([4096, 1, 700], 9)])
+def test_fp8_chain(lens, splits):
+    w = W.make("fp8_h16_b128", B=len(lens), lens=lens)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res)
