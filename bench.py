@@ -1,0 +1,209 @@
+"""Benchmark: one decode step of absorbed MLA (absorb_q, cache_append, decode,
+up_v) over a paged latent KV cache on one MI355X.
+
+Default workload: DeepSeek-V2 shapes (n_h = 128, d_h = 128, d_c = 512,
+d_R = 64), batch 16, 4096 cached tokens per sequence, 64-token pages, bf16.
+Each step appends the current token of every sequence, then attends over its
+whole cache (history plus current).  Caches and weights are replicated and
+rotated per step (like consecutive layers) so that the 256 MB Infinity Cache
+cannot hold the working set; every input is resident in HBM before timing.
+
+Prints one JSON line (see the repository documentation for the fields).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MLA decode: latent-KV GB/s + TFLOP/s as % of roofline, 128 heads, B=16×4K bf16"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="v2_b16_4k")
+    p.add_argument("--splits", type=int, default=0)
+    p.add_argument("--min-replica-mb", type=float, default=600.0)
+    p.add_argument("--cpu-sample-seqs", type=int, default=2)
+    p.add_argument("--no-cpu", action="store_true")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mla_inputs as W
+    import mla_latent_kv_38_amd as mla
+
+    dev = torch.device("cuda:0")
+    w = W.make(args.workload)
+    B, nh, D = w.B, w.n_h, w.D
+    act = torch.bfloat16 if w.act == "bf16" else torch.float32
+    d = mla.make_dims(w.n_h, w.d_h, w.d_c, w.d_R, w.block_size, act=w.act, kv=w.kv,
+                      softmax_scale=w.scale, rope_base=w.rope_base)
+    esz = 1 if w.kv == "e4m3" else (2 if w.kv == "bf16" else 4)
+    row_bytes = D * esz + (4 if w.kv == "e4m3" else 0)
+    cache_bytes = w.num_pages * w.block_size * row_bytes
+    weight_bytes = 2 * nh * w.d_h * w.d_c * (2 if w.act == "bf16" else 4)
+    R = max(1, math.ceil(args.min_replica_mb * 1e6 / (cache_bytes + weight_bytes)))
+
+    def g(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev).to(dt)
+
+    # history (all but the current token) goes into every replica's cache
+    hist_c = np.concatenate([w.c_kv[b][:-1] for b in range(B)])
+    hist_k = np.concatenate([w.k_r[b][:-1] for b in range(B)])
+    hist_pos = np.concatenate([np.arange(w.lens[b] - 1) for b in range(B)]).astype(np.int32)
+    hist_slot = np.concatenate([w.slots(b, 0, int(w.lens[b]) - 1) for b in range(B)])
+    cur_c = np.stack([w.c_kv[b][-1] for b in range(B)])
+    cur_k = np.stack([w.k_r[b][-1] for b in range(B)])
+    cur_pos = (w.lens - 1).astype(np.int32)
+    cur_slot = np.array([w.slots(b, int(w.lens[b]) - 1)[0] for b in range(B)], dtype=np.int64)
+
+    t_hist = (g(hist_c, act), g(hist_k, act), g(hist_pos, torch.int32), g(hist_slot, torch.int64))
+    cur = (g(cur_c, act), g(cur_k, act), g(cur_pos, torch.int32), g(cur_slot, torch.int64))
+    q_c, q_r = g(w.q_c, act), g(w.q_r, act)
+    q_pos = g(w.q_pos, torch.int32)
+    bt, lens = g(w.block_table, torch.int32), g(w.lens, torch.int32)
+    w_uk0, w_uv0 = g(w.w_uk, act), g(w.w_uv, act)
+
+    reps = []
+    fill_ms = []
+    for r in range(R):
+        if w.kv == "e4m3":
+            cache = torch.zeros((w.num_pages, w.block_size, D), dtype=torch.uint8, device=dev)
+            scale = torch.ones((w.num_pages, w.block_size), dtype=torch.float32, device=dev)
+        else:
+            cache = torch.zeros((w.num_pages, w.block_size, D), dtype=act, device=dev)
+            scale = None
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        mla.cache_append(d, *t_hist, cache, scale)
+        e1.record()
+        torch.cuda.synchronize()
+        fill_ms.append(e0.elapsed_time(e1))
+        reps.append(dict(cache=cache, scale=scale, w_uk=w_uk0.clone(), w_uv=w_uv0.clone()))
+    ws = torch.empty(mla.decode_workspace_bytes(d, B, args.splits), dtype=torch.uint8, device=dev)
+    q_abs = torch.empty((B, nh, D), dtype=act, device=dev)
+    o_lat = torch.empty((B, nh, w.d_c), dtype=act, device=dev)
+    lse = torch.empty((B, nh), dtype=torch.float32, device=dev)
+    out = torch.empty((B, nh, w.d_h), dtype=act, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        rp = reps[i % R]
+        mla.absorb_q(d, q_c, q_r, q_pos, rp["w_uk"], q_abs)
+        mla.cache_append(d, *cur, rp["cache"], rp["scale"])
+        if ev is not None:
+            ev[0].record(stream)
+        mla.decode(d, q_abs, rp["cache"], bt, lens, kv_scale=rp["scale"], num_splits=args.splits,
+                   workspace=ws, o_lat=o_lat, lse=lse)
+        if ev is not None:
+            ev[1].record(stream)
+        mla.up_v(d, o_lat, rp["w_uv"], out)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_step = ms_total / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    dec_us = float(np.mean(dec_ms) * 1e3)
+
+    # algorithmic work of one decode call
+    toks = int(w.lens.sum())
+    kv_bytes = toks * row_bytes
+    q_bytes = B * nh * D * (2 if w.act == "bf16" else 4)
+    o_bytes = B * nh * w.d_c * (2 if w.act == "bf16" else 4) + B * nh * 4
+    dec_bytes = kv_bytes + q_bytes + o_bytes
+    flops_tok = 2 * nh * D + 2 * nh * w.d_c
+    dec_flops = toks * flops_tok
+    ach_gbps = dec_bytes / (dec_us * 1e-6) / 1e9
+    ach_tflops = dec_flops / (dec_us * 1e-6) / 1e12
+    ai = dec_flops / dec_bytes
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    if ai < ridge:
+        roof = dict(bound="hbm", achieved=round(ach_gbps, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
+                    frac=round(ach_gbps / HBM_PEAK_GBPS, 4))
+    else:
+        roof = dict(bound="mfma", achieved=round(ach_tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach_tflops / BF16_PEAK_TFLOPS, 4))
+    roof.update(traffic=None, kernel="mla_decode (split + combine)", algorithmic_bytes=dec_bytes,
+                algorithmic_flops=dec_flops, avg_us=round(dec_us, 3),
+                tflops=round(ach_tflops, 1), tflops_frac=round(ach_tflops / BF16_PEAK_TFLOPS, 4))
+
+    step_kv_gbps = kv_bytes / (ms_step * 1e-3) / 1e9
+
+    res = {
+        "metric": METRIC, "value": round(step_kv_gbps, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "seq_len": int(w.lens.max()),
+                   "total_tokens": toks, "n_heads": nh, "d_head": w.d_h, "d_latent": w.d_c,
+                   "d_rope": w.d_R, "block_size": w.block_size, "kv_dtype": w.kv,
+                   "replicas": R, "num_splits": args.splits},
+        "steps_per_s": round(1e3 / ms_step, 1),
+        "step_tflops": round(dec_flops / (ms_step * 1e-3) / 1e12, 1),
+        "decode_us": round(dec_us, 3),
+        "roofline": roof,
+        "cache_fill_GBps": round(cache_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
+    }
+
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, row_bytes)
+    print(json.dumps(res))
+
+
+def cpu_baseline(w, nseq, row_bytes):
+    """The float64 oracle (explicit k_C / v reconstruction) timed on host cores
+    on a bounded sample of the same workload (the first nseq sequences, all heads)."""
+    from oracle import mla_oracle as O
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+    nseq = min(nseq, w.B)
+    toks = int(w.lens[:nseq].sum())
+    t0 = time.perf_counter()
+    for b in range(nseq):
+        O.explicit_decode(w.q_c[b], w.q_r[b], w.c_kv[b], w.k_r[b], w.w_uk, w.w_uv,
+                          scale=w.scale, base=w.rope_base)
+    dt = time.perf_counter() - t0
+    return {"value": round(toks * row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": min(threads, cores),
+            "kind": "oracle", "sample": f"{nseq} of {w.B} sequences ({toks} tokens, all {w.n_h} heads), "
+                                        f"{dt:.2f} s"}
+
+
+if __name__ == "__main__":
+    main()

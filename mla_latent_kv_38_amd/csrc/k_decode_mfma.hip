@@ -1,15 +1,391 @@
-// MFMA decode kernel for DeepSeek-V2 shapes (placeholder until written).
+// MFMA decode for DeepSeek-V2 shapes: d_c = 512, d_R = 64 (rows of 576),
+// 64-token pages, bfloat16 queries and cache, n_h a multiple of 64.
+//
+// Work decomposition.  The batch's pages are flattened and cut into parts
+// (see mla_device.h); one workgroup handles one part for 64 heads.  A
+// workgroup is 4 waves on one CU; it streams its pages HBM -> LDS with
+// direct-to-LDS loads (double-buffered) and every latent row is read from LDS
+// by all 64 heads:
+//   QK  wave w scores head block hb = w & 1 (32 heads) against token half
+//       th = w >> 1 of the page: S^T[32 tok x 32 heads] = C[32 x 576] Q^T,
+//       36 MFMA 32x32x16 bf16, Q^T resident in registers.
+//   softmax  per head (one lane), page max shared between the two token-half
+//       waves through LDS; the reference max only moves when the page max
+//       exceeds it by 2^8 (scores are in log2 units), so rescaling the
+//       accumulators is rare; P is written to LDS as bf16.
+//   PV  wave w accumulates O^T[128 latent columns x 64 heads] =
+//       V^T[128 x 64 tok] P^T[64 tok x 64 heads]: 32 MFMAs per page; V^T
+//       comes from the row-major tile through ds_read_b64_tr_b16, each V
+//       fragment feeding two head blocks.
+// LDS rows are padded to 73 x 16 B so that the QK reads (16 rows, same
+// 16-B column per phase) and the transposed PV reads (4 rows 4 apart x 32
+// columns per phase) are free of bank conflicts; the token order inside each
+// MFMA is permuted to match (it is a contraction index, so any order is exact).
 #include "mla_device.h"
 #include "mla_internal.h"
 
 namespace mla {
+namespace {
 
-bool mfma_decode_supported(const mla_dims& d) { (void)d; return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+#define LDSP __attribute__((address_space(3)))
 
-hipError_t launch_decode_mfma(const mla_dims&, const DecodePlan&, int32_t, const void*, const void*,
-                              const float*, const int32_t*, int32_t, const int32_t*, float*, float*,
-                              void*, float*, hipStream_t) {
-  return hipErrorNotSupported;
+constexpr int kD = 576;
+constexpr int kDc = 512;
+constexpr int kBs = 64;
+constexpr int kRowB = 1168;                 // 1152 data bytes + 16 pad (73 x 16 B)
+constexpr int kPageB = kBs * kRowB;         // 74752 = 73 x 1 KiB
+constexpr int kPtRowB = 144;                // P^T row: 64 bf16 + 16 pad
+constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// Copy one 64-token page (64 x 1152 B) into the padded LDS tile: 73 direct
+// loads of 64 lanes x 16 B; LDS slot s = 64 k + lane holds row s / 73, 16-B
+// chunk s % 73 (chunk 72 is padding and re-reads chunk 0).  Wave w issues
+// loads k = w, w + 4, ...; the lane's (row, chunk) advances by 256 slots
+// = 3 rows + 37 chunks per load.
+struct DmaWalk {
+  int row, ch;
+  __device__ __forceinline__ void start(int wave, int lane) {
+    const int s0 = 64 * wave + lane;
+    row = s0 / 73;
+    ch = s0 - 73 * row;
+  }
+  __device__ __forceinline__ void issue(const char* __restrict__ src, LDSP char* dst, int k) {
+    const unsigned off = static_cast<unsigned>(row * (kD * 2) + (ch == 72 ? 0 : ch * 16));
+    __builtin_amdgcn_global_load_lds(src + off, dst + 1024 * k, 16, 0, 0);
+    ch += 37;
+    row += 3;
+    if (ch >= 73) { ch -= 73; row += 1; }
+  }
+};
+
+__device__ __forceinline__ int dma_count(int wave) { return wave == 0 ? 19 : 18; }
+
+// S^T[32 tokens x 32 heads] = C[32 x 576] . Q^T for one wave: 36 MFMAs fed
+// from LDS four fragments ahead, Q^T read straight from AGPRs.  With kDma the
+// wave's share of the next page's direct loads is spread over the MFMAs.
+template <bool kDma>
+__device__ __forceinline__ f32x16 qk_page(const LDSP char* __restrict__ ap, const bf16x8 (&qf)[36],
+                                          const DmaWalk& walk0, const char* nsrc,
+                                          LDSP char* __restrict__ nbuf, int wave) {
+  f32x16 S;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) S[r] = 0.f;
+  DmaWalk w = walk0;
+  asm volatile("" : "+v"(w.row), "+v"(w.ch));   // keep the address walk inside the loop (no hoisting)
+  constexpr int kPre = 4;
+  bf16x8 af[kPre];
+#pragma unroll
+  for (int kb = 0; kb < kPre; ++kb) af[kb] = *(const LDSP bf16x8*)(ap + 32 * kb);
+#pragma unroll
+  for (int kb = 0; kb < 36; ++kb) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(af[kb % kPre]), "a"(qf[kb]));
+    if (kb + kPre < 36) af[kb % kPre] = *(const LDSP bf16x8*)(ap + 32 * (kb + kPre));
+    if (kDma && (kb & 1) == 0) w.issue(nsrc, nbuf, wave + 4 * (kb >> 1));
+  }
+  if (kDma && wave == 0) w.issue(nsrc, nbuf, 4 * 18);
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 3" ::: "memory");       // MFMA result -> VALU
+  return S;
+}
+
+// Two page buffers, the P^T tile and the exchange area are separate LDS
+// objects: with every buffer reference static, the compiler can tell the
+// next page's direct loads never alias the current page's reads and adds no
+// waits of its own.
+__shared__ __attribute__((aligned(1024))) char g_page0[kPageB];
+__shared__ __attribute__((aligned(1024))) char g_page1[kPageB];
+__shared__ __attribute__((aligned(16))) char g_pt[64 * kPtRowB];
+__shared__ __attribute__((aligned(16))) float g_xm[2 * 64];   // page max per token half
+__shared__ __attribute__((aligned(16))) float g_xa[64];       // alpha per head
+__shared__ __attribute__((aligned(16))) float g_xl[2 * 64];   // row sums per token half
+__shared__ __attribute__((aligned(16))) float g_xf[64];       // final reference max
+
+struct Lane {                      // per-lane constants
+  int wave, lane, l32, hi, hb, th;
+  int a_off, pt_row, tr_off;
+};
+
+struct Acc {                       // per-segment running state of one wave
+  f32x16 o[4][2];
+  float m_ref, l_own;
+};
+
+// One page: QK (+ the next page's loads), softmax, PV.
+// buf (read) and nbuf (direct-load target) are __restrict__: the compiler
+// then knows the in-flight loads into nbuf never alias reads of buf and adds
+// no waits of its own (the explicit vmcnt + barrier at the top orders them).
+__device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict__ buf,
+                                          LDSP char* __restrict__ nbuf,
+                                          bool dma, const char* nsrc, const DmaWalk& walk0,
+                                          const bf16x8 (&qf)[36], int nvalid, float s2, Acc& acc) {
+  LDSP char* pt = (LDSP char*)g_pt;
+  float* xm = g_xm;
+  float* xa = g_xa;
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();                                               // this page landed; previous one consumed
+
+  f32x16 S = dma ? qk_page<true>(buf + ln.a_off, qf, walk0, nsrc, nbuf, ln.wave)
+                 : qk_page<false>(buf + ln.a_off, qf, walk0, nsrc, nbuf, ln.wave);
+
+  float mloc = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int ra = r >> 2;
+    const int t = 32 * ln.th + 16 * (ra >> 1) + 2 * (ra & 1) + ln.hi + 4 * (r & 3);
+    const float v = t < nvalid ? S[r] * s2 : -INFINITY;
+    S[r] = v;
+    mloc = fmaxf(mloc, v);
+  }
+  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  if (ln.hi == 0) xm[ln.th * 64 + ln.hb * 32 + ln.l32] = mloc;
+  __syncthreads();                                               // page maxima exchanged
+
+  const float mpage = fmaxf(mloc, xm[(1 - ln.th) * 64 + ln.hb * 32 + ln.l32]);
+  float alpha = 1.f;
+  if (mpage > acc.m_ref + kTau) {
+    alpha = __builtin_amdgcn_exp2f(acc.m_ref - mpage);
+    acc.m_ref = mpage;
+  }
+  float ps = 0.f;
+  uint32_t pk[8];
+#pragma unroll
+  for (int r = 0; r < 16; r += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(S[r] - acc.m_ref);
+    const float p1 = __builtin_amdgcn_exp2f(S[r + 1] - acc.m_ref);
+    ps += p0 + p1;
+    pk[r >> 1] = pack_bf16(p0, p1);
+  }
+  acc.l_own = acc.l_own * alpha + ps;
+  if (ln.th == 0 && ln.hi == 0) xa[ln.hb * 32 + ln.l32] = alpha;
+#pragma unroll
+  for (int ra = 0; ra < 4; ++ra) {
+    const int slot = 16 * (2 * ln.th + (ra >> 1)) + 4 * (2 * (ra & 1) + ln.hi);
+    *(LDSP u32x2*)(pt + ln.pt_row + slot * 2) = u32x2{pk[2 * ra], pk[2 * ra + 1]};
+  }
+  if (nvalid < kBs) {                                            // rows past the end: zero the latent
+    for (int i = threadIdx.x; i < (kBs - nvalid) * 64; i += 256) {
+      const int row = nvalid + (i >> 6), ch = i & 63;
+      *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  __syncthreads();                                               // P^T and alpha visible
+
+  // ---- PV: 16 steps (k-step ks, column block cb), one step of prefetch ------
+  const float al0 = xa[ln.l32], al1 = xa[32 + ln.l32];
+  if (__any(al0 != 1.f || al1 != 1.f)) {
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) { acc.o[cb][0][r] *= al0; acc.o[cb][1][r] *= al1; }
+    asm volatile("s_nop 2" ::: "memory");                        // VALU -> MFMA source
+  }
+  const LDSP char* vbase = buf + ln.tr_off;
+  auto vload = [&](int step) {
+    const int ks = step >> 2, cb = step & 3;
+    const LDSP char* vp = vbase + 16 * ks * kRowB + 64 * cb;
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)vp);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + kRowB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  auto pload = [&](int ks, int h2) {
+    return *(const LDSP bf16x8*)(pt + (32 * h2 + ln.l32) * kPtRowB + (16 * ks + 8 * ln.hi) * 2);
+  };
+  bf16x8 vcur = vload(0);
+  bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
+  bf16x8 pn0 = pc0, pn1 = pc1;
+#pragma unroll
+  for (int step = 0; step < 16; ++step) {
+    const int cb = step & 3;
+    bf16x8 vnext = vcur;
+    if (step + 1 < 16) vnext = vload(step + 1);
+    if (cb == 0 && step + 4 < 16) { pn0 = pload((step >> 2) + 1, 0); pn1 = pload((step >> 2) + 1, 1); }
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n"
+                 "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+                 : "+v"(acc.o[cb][0]), "+v"(acc.o[cb][1]) : "v"(vcur), "v"(pc0), "v"(pc1));
+    vcur = vnext;
+    if (cb == 3) { pc0 = pn0; pc1 = pn1; }
+  }
+}
+
+__global__ void __launch_bounds__(256, 1) decode_mfma_h64(
+    int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2,
+    const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
+    const int32_t* __restrict__ block_table, int32_t max_pages, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat,
+    float* __restrict__ lse) {
+  Lane ln;
+  const int tid = threadIdx.x;
+  ln.lane = tid & 63;
+  ln.wave = __builtin_amdgcn_readfirstlane(tid >> 6);          // uniform within the wave
+  ln.l32 = ln.lane & 31;
+  ln.hi = ln.lane >> 5;
+  ln.hb = ln.wave & 1;
+  ln.th = ln.wave >> 1;
+
+  // Workgroups 8 apart run on the same XCD: the HG head groups of one part
+  // are placed there so their page reads share that XCD's L2.
+  const int grp = blockIdx.x / (8 * HG), within = blockIdx.x % (8 * HG);
+  const int hg = within / 8;
+  const int part = grp * 8 + within % 8;
+  if (part >= W) return;
+
+  int32_t* scan = reinterpret_cast<int32_t*>(g_pt);
+  int32_t chunk;
+  page_prefix(seq_lens, B, kBs, scan, &chunk);
+  const int64_t P = scan[blockDim.x];
+  const int64_t x1 = part_start(part + 1, P, W);
+  int64_t x = part_start(part, P, W);
+  if (x >= x1) return;
+  int32_t b;
+  int64_t first;
+  locate_page(seq_lens, B, kBs, scan, chunk, x, &b, &first);
+  __syncthreads();
+
+  // QK A operand: lane reads token row tok(l32) of its half, 16-B chunk hi of each k-step
+  {
+    const int i = ln.l32, a = i >> 3, q = i & 3, bq = (i >> 2) & 1;
+    const int tok = 32 * ln.th + 16 * (a >> 1) + 2 * (a & 1) + bq + 4 * q;
+    ln.a_off = tok * kRowB + ln.hi * 16;
+  }
+  ln.pt_row = (ln.hb * 32 + ln.l32) * kPtRowB;
+  {
+    const int g = ln.lane >> 4, sg = ln.lane & 15;             // PV transposed reads
+    ln.tr_off = (4 * (sg >> 2) + 2 * ln.hi) * kRowB + (128 * ln.wave + 16 * (g & 1) + 4 * (sg & 3)) * 2;
+  }
+
+  DmaWalk walk0;
+  walk0.start(ln.wave, ln.lane);
+  const int ndma = dma_count(ln.wave);
+  const char* cbase = reinterpret_cast<const char*>(cache);
+  constexpr int64_t kPageBytesG = (int64_t)kBs * kD * 2;
+
+  for (;;) {
+    const int32_t L = seq_lens[b];
+    const int64_t np = pages_of(L, kBs);
+    const int64_t jp0 = x - first;
+    const int64_t jp1 = min(np, jp0 + (x1 - x));
+    const int32_t* bt = block_table + (int64_t)b * max_pages;
+
+    // First page into buffer 0 and this head group's 64 absorbed query rows
+    // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer 1.
+    {
+      DmaWalk w = walk0, wq = walk0;
+      const char* src = cbase + (int64_t)bt[jp0] * kPageBytesG;
+      const char* qsrc = reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD);
+      for (int i = 0; i < ndma; ++i) w.issue(src, (LDSP char*)g_page0, ln.wave + 4 * i);
+      for (int i = 0; i < ndma; ++i) wq.issue(qsrc, (LDSP char*)g_page1, ln.wave + 4 * i);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    // Q^T fragments stay in AGPRs for the whole segment (the MFMAs read them there)
+    bf16x8 qf[36];
+    {
+      const LDSP char* qrow = (LDSP char*)g_page1 + (ln.hb * 32 + ln.l32) * kRowB + ln.hi * 16;
+      bf16x8 t[36];
+#pragma unroll
+      for (int kb = 0; kb < 36; ++kb) t[kb] = *(const LDSP bf16x8*)(qrow + 32 * kb);
+#pragma unroll
+      for (int kb = 0; kb < 36; ++kb) asm volatile("" : "=a"(qf[kb]) : "0"(t[kb]));
+    }
+    __syncthreads();                                             // buffer 1 free again
+
+    Acc acc;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc.o[cb][h2][r] = 0.f;
+    acc.m_ref = -INFINITY;
+    acc.l_own = 0.f;
+
+    for (int64_t jp = jp0; jp < jp1; ++jp) {
+      const bool even = ((jp - jp0) & 1) == 0;
+      LDSP char* buf = even ? (LDSP char*)g_page0 : (LDSP char*)g_page1;
+      LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
+      const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - jp * kBs);
+      const bool more = jp + 1 < jp1;
+      page_step(ln, buf, nbuf, more, cbase + (int64_t)bt[more ? jp + 1 : jp] * kPageBytesG,
+                walk0, qf, nvalid, s2, acc);
+    }
+
+    // ---- segment epilogue: normalise and store ------------------------------
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 3" ::: "memory");   // MFMA result -> VALU
+    __syncthreads();
+    const float l_lane = acc.l_own + __shfl_xor(acc.l_own, 32);
+    if (ln.hi == 0) {
+      g_xl[ln.th * 64 + ln.hb * 32 + ln.l32] = l_lane;
+      if (ln.th == 0) g_xf[ln.hb * 32 + ln.l32] = acc.m_ref;
+    }
+    __syncthreads();
+    const bool whole = (jp0 == 0 && jp1 == np);
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      const int hh = h2 * 32 + ln.l32;
+      const float lt = g_xl[hh] + g_xl[64 + hh];
+      const float inv = 1.f / lt;
+      const float lse_v = (g_xf[hh] + __log2f(lt)) * 0.69314718055994531f;
+      const int64_t head = (int64_t)hg * 64 + hh;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int col = 128 * ln.wave + 32 * cb + 8 * q4 + 4 * ln.hi;
+          const float o0 = acc.o[cb][h2][4 * q4] * inv, o1 = acc.o[cb][h2][4 * q4 + 1] * inv;
+          const float o2 = acc.o[cb][h2][4 * q4 + 2] * inv, o3 = acc.o[cb][h2][4 * q4 + 3] * inv;
+          if (whole) {
+            *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
+                u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+          } else {
+            *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + head) * kDc + col) =
+                f32x4{o0, o1, o2, o3};
+          }
+        }
+      if (ln.wave == 0 && ln.hi == 0) {
+        if (whole) { if (lse) lse[(int64_t)b * n_h + head] = lse_v; }
+        else ws_lse[((int64_t)part + b) * n_h + head] = lse_v;
+      }
+    }
+
+    x += jp1 - jp0;
+    if (x >= x1) break;
+    do { ++b; } while (pages_of(seq_lens[b], kBs) == 0);
+    first = x;
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+bool mfma_decode_supported(const mla_dims& d) {
+  return d.act_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_latent == kDc && d.d_rope == 64 &&
+         d.block_size == kBs && d.n_heads % 64 == 0;
+}
+
+hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
+                              const void* q_abs, const void* cache, const float* kv_scale,
+                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, float* ws_o, float* ws_lse, void* o_lat,
+                              float* lse, hipStream_t s) {
+  (void)kv_scale;
+  const int HG = d.n_heads / 64;
+  const int W = plan.parts;
+  const int grid = ((W + 7) / 8) * 8 * HG;
+  const float s2 = d.softmax_scale * 1.4426950408889634f;
+  decode_mfma_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
+                                       static_cast<const uint16_t*>(cache), block_table, max_pages,
+                                       seq_lens, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
+  return launch_combine(d, plan, B, seq_lens, ws_o, ws_lse, o_lat, lse, s);
 }
 
 }  // namespace mla

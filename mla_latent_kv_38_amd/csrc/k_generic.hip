@@ -226,57 +226,96 @@ __global__ void __launch_bounds__(256) decode_generic(
 
 // ---------------------------------------------------------------------------
 // combine: log-sum-exp merge of a sequence's segment partials.
-// grid (B, n_h), block 128.  Sequences with a single segment were written by
-// the decode kernel; empty sequences get o_lat = 0, lse = -inf here.
+// grid (B, n_h), block 64 (one wave); lane handles 4-column groups of the
+// latent row.  Sequences with a single segment were written by the decode
+// kernel; empty sequences get o_lat = 0, lse = -inf here.
 // ---------------------------------------------------------------------------
+constexpr int kCombMaxSeg = 64;   // segments merged per pass (more are folded in passes)
+
 template <typename TO>
-__global__ void __launch_bounds__(128) combine_kernel(int32_t B, int32_t n_h, int32_t d_c, int32_t bs,
-                                                      int32_t W, const int32_t* __restrict__ seq_lens,
-                                                      const float* __restrict__ ws_o,
-                                                      const float* __restrict__ ws_lse,
-                                                      TO* __restrict__ o_lat, float* __restrict__ lse) {
-  __shared__ int64_t red[2][128];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+__global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int32_t d_c, int32_t bs,
+                                                     int32_t W, const int32_t* __restrict__ seq_lens,
+                                                     const float* __restrict__ ws_o,
+                                                     const float* __restrict__ ws_lse,
+                                                     TO* __restrict__ o_lat, float* __restrict__ lse) {
+  __shared__ float wgt[kCombMaxSeg];
+  __shared__ int32_t slot[kCombMaxSeg];
+  const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   int64_t pre = 0, tot = 0;
-  for (int i = tid; i < B; i += blockDim.x) {
-    int64_t np = pages_of(seq_lens[i], bs);
+  for (int i = lane; i < B; i += 64) {
+    const int64_t np = pages_of(seq_lens[i], bs);
     tot += np;
     if (i < b) pre += np;
   }
-  red[0][tid] = pre;
-  red[1][tid] = tot;
-  __syncthreads();
-  for (int s = 64; s > 0; s >>= 1) {
-    if (tid < s) { red[0][tid] += red[0][tid + s]; red[1][tid] += red[1][tid + s]; }
-    __syncthreads();
+  for (int off = 32; off > 0; off >>= 1) {
+    pre += __shfl_xor(pre, off);
+    tot += __shfl_xor(tot, off);
   }
-  pre = red[0][0];
-  const int64_t P = red[1][0];
+  const int64_t P = tot;
   const int64_t np = pages_of(seq_lens[b], bs);
   const int64_t row = (int64_t)b * n_h + h;
   if (np == 0) {
-    for (int c = tid; c < d_c; c += blockDim.x) io<TO>::store(o_lat, row * d_c + c, 0.f);
-    if (tid == 0 && lse) lse[row] = -INFINITY;
+    for (int c = lane; c < d_c; c += 64) io<TO>::store(o_lat, row * d_c + c, 0.f);
+    if (lane == 0 && lse) lse[row] = -INFINITY;
     return;
   }
   const int64_t w0 = part_of_page(pre, P, W), w1 = part_of_page(pre + np - 1, P, W);
   if (w0 == w1) return;
-  // parts strictly inside [w0, w1] may be empty (more parts than pages): skip them
+  // reference max over the non-empty parts (parts inside [w0, w1] can be empty
+  // when there are more parts than pages)
   float M = -INFINITY;
-  for (int64_t w = w0; w <= w1; ++w)
+  for (int64_t w = w0 + lane; w <= w1; w += 64)
     if (part_start(w, P, W) < part_start(w + 1, P, W)) M = fmaxf(M, ws_lse[(w + b) * n_h + h]);
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
   float denom = 0.f;
-  for (int64_t w = w0; w <= w1; ++w)
-    if (part_start(w, P, W) < part_start(w + 1, P, W)) denom += expf(ws_lse[(w + b) * n_h + h] - M);
+  const int ncol4 = (d_c % 4 == 0) ? d_c / 4 : 0;   // float4 path needs 16-byte rows
+  float4 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int64_t base = w0; base <= w1; base += kCombMaxSeg) {
+    const int nseg = (int)min<int64_t>(kCombMaxSeg, w1 + 1 - base);
+    __syncthreads();
+    if (lane < nseg) {
+      const int64_t w = base + lane;
+      const bool live = part_start(w, P, W) < part_start(w + 1, P, W);
+      wgt[lane] = live ? expf(ws_lse[(w + b) * n_h + h] - M) : 0.f;
+      slot[lane] = (int32_t)(w + b);
+    }
+    __syncthreads();
+    for (int k = 0; k < nseg; ++k) {
+      const float wk = wgt[k];
+      denom += wk;
+      if (wk == 0.f) continue;
+      const float4* src = reinterpret_cast<const float4*>(ws_o + ((int64_t)slot[k] * n_h + h) * d_c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c4 = lane + 64 * j;
+        if (c4 < ncol4) {
+          const float4 v = src[c4];
+          acc[j].x += wk * v.x; acc[j].y += wk * v.y; acc[j].z += wk * v.z; acc[j].w += wk * v.w;
+        }
+      }
+    }
+  }
   const float inv = 1.f / denom;
-  for (int c = tid; c < d_c; c += blockDim.x) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c4 = lane + 64 * j;
+    if (c4 < ncol4) {
+      io<TO>::store(o_lat, row * d_c + 4 * c4 + 0, acc[j].x * inv);
+      io<TO>::store(o_lat, row * d_c + 4 * c4 + 1, acc[j].y * inv);
+      io<TO>::store(o_lat, row * d_c + 4 * c4 + 2, acc[j].z * inv);
+      io<TO>::store(o_lat, row * d_c + 4 * c4 + 3, acc[j].w * inv);
+    }
+  }
+  for (int c = 4 * ncol4 + lane; c < d_c; c += 64) {       // d_c not a multiple of 4
     float o = 0.f;
     for (int64_t w = w0; w <= w1; ++w)
       if (part_start(w, P, W) < part_start(w + 1, P, W))
         o += expf(ws_lse[(w + b) * n_h + h] - M) * ws_o[((w + b) * n_h + h) * d_c + c];
     io<TO>::store(o_lat, row * d_c + c, o * inv);
   }
-  if (tid == 0 && lse) lse[row] = M + logf(denom);
+  if (lane == 0 && lse) lse[row] = M + logf(denom);
 }
 
 // ---------------------------------------------------------------------------
@@ -343,6 +382,18 @@ hipError_t launch_cache_append(const mla_dims& d, int32_t T_, const void* c_kv, 
   return hipGetLastError();
 }
 
+hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
+                          const float* ws_o, const float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
+  dim3 grid(B, d.n_heads);
+  if (d.act_dtype == MLA_F32)
+    combine_kernel<float><<<grid, 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts, seq_lens,
+                                               ws_o, ws_lse, static_cast<float*>(o_lat), lse);
+  else
+    combine_kernel<bf16_t><<<grid, 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts, seq_lens,
+                                                ws_o, ws_lse, static_cast<bf16_t*>(o_lat), lse);
+  return hipGetLastError();
+}
+
 template <typename TQ>
 static void decode_generic_dispatch(const mla_dims& d, const DecodePlan& plan, int32_t B,
                                     const void* q_abs, const void* cache, const float* kv_scale,
@@ -360,7 +411,7 @@ static void decode_generic_dispatch(const mla_dims& d, const DecodePlan& plan, i
   else
     decode_generic<TQ, MLA_E4M3><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
         d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, ws_o, ws_lse, o, lse);
-  combine_kernel<TQ><<<dim3(B, d.n_heads), 128, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts,
+  combine_kernel<TQ><<<dim3(B, d.n_heads), 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts,
       seq_lens, ws_o, ws_lse, o, lse);
 }
 
@@ -394,7 +445,11 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
                          float* lse, hipStream_t s) {
   float *ws_o, *ws_lse;
   workspace_split(d, plan, B, ws, &ws_o, &ws_lse);
-  if (plan.mfma)
+  // the MFMA kernel loads 16-byte fragments and stores 8-byte groups
+  const bool aligned = (reinterpret_cast<uintptr_t>(q_abs) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(cache) % 16 == 0) &&
+                       (reinterpret_cast<uintptr_t>(o_lat) % 8 == 0);
+  if (plan.mfma && aligned)
     return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
                               ws_o, ws_lse, o_lat, lse, s);
   if (d.act_dtype == MLA_F32)

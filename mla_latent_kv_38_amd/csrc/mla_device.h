@@ -86,23 +86,32 @@ __device__ __forceinline__ int64_t part_of_page(int64_t x, int64_t P, int64_t W)
 __device__ __forceinline__ int32_t pages_of(int32_t L, int32_t bs) { return (L + bs - 1) / bs; }
 
 // Block-wide page prefix over sequences.  `scan` is __shared__ scratch of
-// blockDim.x + 1 ints.  After the call scan[t] = pages of sequences before
-// thread t's chunk [t*chunk, (t+1)*chunk) and scan[blockDim.x] = total P.
+// blockDim.x + 1 ints (blockDim.x a multiple of 64, at most 1024).  After the
+// call scan[t] = pages of sequences before thread t's chunk
+// [t*chunk, (t+1)*chunk) and scan[blockDim.x] = total P.
 __device__ __forceinline__ void page_prefix(const int32_t* seq_lens, int32_t B, int32_t bs,
                                             int32_t* scan, int32_t* chunk_out) {
-  const int nt = blockDim.x, t = threadIdx.x;
+  __shared__ int32_t wave_tot[16];
+  const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int32_t chunk = (B + nt - 1) / nt;
   int32_t s = 0;
   for (int32_t b = t * chunk; b < min(B, (t + 1) * chunk); ++b) s += pages_of(seq_lens[b], bs);
-  scan[t + 1] = s;
-  if (t == 0) scan[0] = 0;
-  __syncthreads();
-  if (t == 0) {
-    for (int i = 1; i <= nt; ++i) scan[i] += scan[i - 1];
+  int32_t v = s;                         // inclusive scan inside the wave
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(v, off);
+    if (lane >= off) v += u;
   }
+  if (lane == 63) wave_tot[wv] = v;
+  __syncthreads();
+  int32_t carry = 0;
+  for (int w = 0; w < wv; ++w) carry += wave_tot[w];
+  scan[t + 1] = v + carry;
+  if (t == 0) scan[0] = 0;
   __syncthreads();
   *chunk_out = chunk;
 }
+
 // Sequence owning flattened page x (0 <= x < P), and that sequence's first page.
 __device__ __forceinline__ void locate_page(const int32_t* seq_lens, int32_t B, int32_t bs,
                                             const int32_t* scan, int32_t chunk, int64_t x,

@@ -29,6 +29,9 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
 hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                        hipStream_t s);
 
+hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
+                          const float* ws_o, const float* ws_lse, void* o_lat, float* lse, hipStream_t s);
+
 // Whether the MFMA decode kernel handles these dims.
 bool mfma_decode_supported(const mla_dims& d);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
