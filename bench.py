@@ -110,15 +110,17 @@ def main():
 
     def step(i, ev=None):
         rp = reps[i % R]
+        rec = (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None)
+        rec(0)
         mla.absorb_q(d, q_c, q_r, q_pos, rp["w_uk"], q_abs)
+        rec(1)
         mla.cache_append(d, *cur, rp["cache"], rp["scale"])
-        if ev is not None:
-            ev[0].record(stream)
+        rec(2)
         mla.decode(d, q_abs, rp["cache"], bt, lens, kv_scale=rp["scale"], num_splits=args.splits,
                    workspace=ws, o_lat=o_lat, lse=lse)
-        if ev is not None:
-            ev[1].record(stream)
+        rec(3)
         mla.up_v(d, o_lat, rp["w_uv"], out)
+        rec(4)
 
     for i in range(args.warmup):
         step(i)
@@ -126,8 +128,7 @@ def main():
 
     # timed region: K whole steps
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
@@ -136,8 +137,9 @@ def main():
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
-    dec_ms = np.array([a.elapsed_time(b) for a, b in evs])
-    dec_us = float(np.mean(dec_ms) * 1e3)
+    call_us = {name: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
+               for k, name in enumerate(["absorb_q", "cache_append", "decode", "up_v"])}
+    dec_us = call_us["decode"]
 
     # algorithmic work of one decode call
     toks = int(w.lens.sum())
@@ -175,6 +177,7 @@ def main():
         "steps_per_s": round(1e3 / ms_step, 1),
         "step_tflops": round(dec_flops / (ms_step * 1e-3) / 1e12, 1),
         "decode_us": round(dec_us, 3),
+        "call_us": {k: round(v, 3) for k, v in call_us.items()},
         "roofline": roof,
         "cache_fill_GBps": round(cache_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
     }

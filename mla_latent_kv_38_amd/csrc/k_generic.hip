@@ -349,6 +349,9 @@ __global__ void __launch_bounds__(256) up_v_generic(int32_t B, int32_t n_h, int3
 // ---------------------------------------------------------------------------
 hipError_t launch_absorb_q(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
                            const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t s) {
+  bool handled = false;
+  hipError_t e = launch_absorb_q_mfma(d, B, q_c, q_r, pos, w_uk, q_abs, s, &handled);
+  if (handled || e != hipSuccess) return e;
   dim3 grid(d.n_heads, (d.d_latent + 255) / 256, (B + kBB - 1) / kBB);
   size_t shm = sizeof(float) * kBB * d.d_head;
   if (d.act_dtype == MLA_F32)
@@ -463,6 +466,9 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
 
 hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                        hipStream_t s) {
+  bool handled = false;
+  hipError_t e = launch_up_v_mfma(d, B, o_lat, w_uv, out, s, &handled);
+  if (handled || e != hipSuccess) return e;
   dim3 grid(d.n_heads, (B + kBB - 1) / kBB);
   size_t shm = sizeof(float) * kBB * d.d_latent;
   if (d.act_dtype == MLA_F32)

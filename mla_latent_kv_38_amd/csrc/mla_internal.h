@@ -32,6 +32,14 @@ hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const vo
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
                           const float* ws_o, const float* ws_lse, void* o_lat, float* lse, hipStream_t s);
 
+// MFMA projections (bf16); *handled = false when the shapes or alignments are
+// not covered, and the caller then runs the generic kernel.
+hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
+                                const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t s,
+                                bool* handled);
+hipError_t launch_up_v_mfma(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
+                            hipStream_t s, bool* handled);
+
 // Whether the MFMA decode kernel handles these dims.
 bool mfma_decode_supported(const mla_dims& d);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
