@@ -109,6 +109,7 @@ __shared__ __attribute__((aligned(16))) float g_xm[2 * 64];   // page max per to
 __shared__ __attribute__((aligned(16))) float g_xa[64];       // alpha per head
 __shared__ __attribute__((aligned(16))) float g_xl[2 * 64];   // row sums per token half
 __shared__ __attribute__((aligned(16))) float g_xf[64];       // final reference max
+__shared__ int32_t g_lens[256];                               // seq_lens, when the batch has <= 256
 
 struct Lane {                      // per-lane constants
   int wave, lane, l32, hi, hb, th;
@@ -232,16 +233,20 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   ln.hb = ln.wave & 1;
   ln.th = ln.wave >> 1;
 
-  // Workgroups 8 apart run on the same XCD: the HG head groups of one part
-  // are placed there so their page reads share that XCD's L2.
-  const int grp = blockIdx.x / (8 * HG), within = blockIdx.x % (8 * HG);
-  const int hg = within / 8;
-  const int part = grp * 8 + within % 8;
+  // Workgroup i runs on XCD i % 8.  XCD x takes the contiguous parts
+  // [x ppx, (x+1) ppx) with all their head groups, so the two head groups of
+  // a part read each page through the same L2, and the parts of one sequence
+  // (which share its query rows) mostly sit on one XCD.
+  const int ppx = (W + 7) / 8;
+  const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int hg = j % HG;
+  const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
   int32_t* scan = reinterpret_cast<int32_t*>(g_pt);
   int32_t chunk;
-  page_prefix(seq_lens, B, kBs, scan, &chunk);
+  page_prefix(seq_lens, B, kBs, scan, &chunk, g_lens);
+  auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
   const int64_t P = scan[blockDim.x];
   const int64_t x1 = part_start(part + 1, P, W);
   int64_t x = part_start(part, P, W);
@@ -270,14 +275,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   constexpr int64_t kPageBytesG = (int64_t)kBs * kD * 2;
 
   for (;;) {
-    const int32_t L = seq_lens[b];
+    const int32_t L = seq_len(b);
     const int64_t np = pages_of(L, kBs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
     const int32_t* bt = block_table + (int64_t)b * max_pages;
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
-    // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer 1.
+    // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
+    // 1, both as whole 1 KiB direct loads.
     {
       DmaWalk w = walk0, wq = walk0;
       const char* src = cbase + (int64_t)bt[jp0] * kPageBytesG;
@@ -346,9 +352,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
           if (whole) {
             *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
                 u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
-          } else {
-            *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + head) * kDc + col) =
-                f32x4{o0, o1, o2, o3};
+          } else {                                               // quad ((w*4+cb)*2+h2)*4+q4: 64 lanes x 16 B
+            const int quad = ((ln.wave * 4 + cb) * 2 + h2) * 4 + q4;
+            *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + (int64_t)hg * 64) * kDc +
+                                      quad * 256 + ln.lane * 4) = f32x4{o0, o1, o2, o3};
           }
         }
       if (ln.wave == 0 && ln.hi == 0) {
@@ -359,9 +366,98 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 
     x += jp1 - jp0;
     if (x >= x1) break;
-    do { ++b; } while (pages_of(seq_lens[b], kBs) == 0);
+    do { ++b; } while (pages_of(seq_len(b), kBs) == 0);
     first = x;
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Merge of the split-KV partials of decode_mfma_h64.  A partial (slot, 64-head
+// group) is 128 KiB in register order: quad ((w*4 + cb)*2 + h2)*4 + q4 holds,
+// for lane l, latent columns 128w + 32cb + 8q4 + 4(l/32) .. +3 of head
+// 32h2 + l%32, already divided by its own row sum; its log-sum-exp is in
+// ws_lse.  Workgroup = (sequence, head group, wave-column block w*4+cb);
+// thread (q4, l) owns two float4 of each partial (h2 = 0, 1).  Parts are
+// merged eight at a time with a running maximum, every load of a batch in
+// flight at once and no LDS or barrier after the page count:
+//   o_lat = sum_k e^(lse_k - M) o_k / sum_k e^(lse_k - M),  lse = M + ln(sum).
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32_t W, int32_t HG,
+                                                   const int32_t* __restrict__ seq_lens,
+                                                   const float* __restrict__ ws_o,
+                                                   const float* __restrict__ ws_lse,
+                                                   uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
+  __shared__ int32_t scan[257];
+  const int tid = threadIdx.x, lane = tid & 63, q4 = tid >> 6, l32 = lane & 31;
+  const int wc = blockIdx.x % 16, hg = (blockIdx.x / 16) % HG, b = blockIdx.x / (16 * HG);
+  if (b >= B) return;
+  int32_t chunk;
+  page_prefix(seq_lens, B, kBs, scan, &chunk);
+  const int64_t P = scan[blockDim.x];
+  int64_t pre = 0;
+  if (chunk == 1) {
+    pre = scan[b];
+  } else {
+    for (int32_t i = 0; i < b; ++i) pre += pages_of(seq_lens[i], kBs);
+  }
+  const int64_t np = pages_of(seq_lens[b], kBs);
+  const int64_t head0 = (int64_t)b * n_h + (int64_t)hg * 64;
+  const int col0 = 128 * (wc >> 2) + 32 * (wc & 3);
+  if (np == 0) {                                   // empty sequence: zero output, lse = -inf
+    for (int i = tid; i < 64 * 8; i += 256) {
+      const int hh = i >> 3, c4 = i & 7;
+      *reinterpret_cast<u32x2*>(o_lat + (head0 + hh) * kDc + col0 + 4 * c4) = u32x2{0u, 0u};
+    }
+    if (wc == 0 && tid < 64 && lse) lse[head0 + tid] = -INFINITY;
+    return;
+  }
+  const int64_t w0 = part_of_page(pre, P, W), w1 = part_of_page(pre + np - 1, P, W);
+  if (w0 == w1) return;                            // one part: written by the decode kernel
+
+  const int off0 = ((wc * 2 + 0) * 4 + q4) * 256 + lane * 4;
+  const int off1 = ((wc * 2 + 1) * 4 + q4) * 256 + lane * 4;
+  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float m0 = -INFINITY, m1 = -INFINITY, d0 = 0.f, d1 = 0.f;
+  for (int64_t base = w0; base <= w1; base += 8) {
+    f32x4 v0[8], v1[8];
+    float e0[8], e1[8];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {               // part w0 always holds a page: dead parts read it
+      const int64_t w = base + jj;
+      const bool live = w <= w1 && part_start(w, P, W) < part_start(w + 1, P, W);
+      const int64_t slot = (live ? w : w0) + b;
+      const float* src = ws_o + (slot * n_h + (int64_t)hg * 64) * kDc;
+      v0[jj] = *reinterpret_cast<const f32x4*>(src + off0);
+      v1[jj] = *reinterpret_cast<const f32x4*>(src + off1);
+      const float* ls = ws_lse + slot * n_h + (int64_t)hg * 64;
+      e0[jj] = live ? ls[l32] : -INFINITY;
+      e1[jj] = live ? ls[32 + l32] : -INFINITY;
+    }
+    float n0 = m0, n1 = m1;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) { n0 = fmaxf(n0, e0[jj]); n1 = fmaxf(n1, e1[jj]); }
+    const float a0 = n0 == m0 ? 1.f : __expf(m0 - n0), a1 = n1 == m1 ? 1.f : __expf(m1 - n1);
+    acc0 *= a0; d0 *= a0; m0 = n0;
+    acc1 *= a1; d1 *= a1; m1 = n1;
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const float x0 = e0[jj] == -INFINITY ? 0.f : __expf(e0[jj] - m0);
+      const float x1 = e1[jj] == -INFINITY ? 0.f : __expf(e1[jj] - m1);
+      d0 += x0; d1 += x1;
+      acc0 += x0 * v0[jj];
+      acc1 += x1 * v1[jj];
+    }
+  }
+  const int col = col0 + 8 * q4 + 4 * (lane >> 5);
+  const float i0 = 1.f / d0, i1 = 1.f / d1;
+  *reinterpret_cast<u32x2*>(o_lat + (head0 + l32) * kDc + col) =
+      u32x2{pack_bf16(acc0[0] * i0, acc0[1] * i0), pack_bf16(acc0[2] * i0, acc0[3] * i0)};
+  *reinterpret_cast<u32x2*>(o_lat + (head0 + 32 + l32) * kDc + col) =
+      u32x2{pack_bf16(acc1[0] * i1, acc1[1] * i1), pack_bf16(acc1[2] * i1, acc1[3] * i1)};
+  if (wc == 0 && tid < 32 && lse) {
+    lse[head0 + l32] = m0 + __logf(d0);
+    lse[head0 + 32 + l32] = m1 + __logf(d1);
   }
 }
 
@@ -380,12 +476,16 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
   (void)kv_scale;
   const int HG = d.n_heads / 64;
   const int W = plan.parts;
-  const int grid = ((W + 7) / 8) * 8 * HG;
+  const int grid = ((W + 7) / 8) * 8 * HG;                  // 8 XCDs x ceil(W/8) parts x HG
   const float s2 = d.softmax_scale * 1.4426950408889634f;
   decode_mfma_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
                                        static_cast<const uint16_t*>(cache), block_table, max_pages,
                                        seq_lens, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
-  return launch_combine(d, plan, B, seq_lens, ws_o, ws_lse, o_lat, lse, s);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, ws_o, ws_lse,
+                                          static_cast<uint16_t*>(o_lat), lse);
+  return hipGetLastError();
 }
 
 }  // namespace mla

@@ -59,6 +59,29 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
   const int g = lane >> 4, s = lane & 15;
   const int64_t D = d_c + d_R;
 
+  // RoPE half of q_abs, pairs spread over the head's workgroups.  The first
+  // pair's inputs are loaded before the weight tile, so its float64 rotation
+  // runs while the tile is in flight (loads complete in order).
+  const int half = d_R / 2;
+  const int stride = cblocks * 256;
+  const int i_first = cb * 256 + tid;
+  const bool has_pair = i_first < B * half;
+  float r0 = 0.f, r1 = 0.f;
+  int32_t rpos = 0;
+  if (has_pair) {
+    const int bb = i_first / half, p = i_first - bb * half;
+    const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
+    r0 = bf16_to_f32(q_r[src]);
+    r1 = bf16_to_f32(q_r[src + 1]);
+    rpos = pos[bb];
+  }
+  auto rope_store = [&](int i, float x0, float x1, int32_t ps) {
+    const int bb = i / half, p = i - bb * half;
+    float y0, y1;
+    rope_pair(x0, x1, ps, p, d_R, base, &y0, &y1);
+    *reinterpret_cast<uint32_t*>(q_abs + ((int64_t)bb * n_h + h) * D + d_c + 2 * p) = pack_bf16(y0, y1);
+  };
+
   // stage W_UK[h][:, c0:c0+128] (d_h rows of 256 B): all loads first, then the LDS writes
   {
     constexpr int kPer = d_h * 16 / 256;
@@ -68,11 +91,17 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
       const int c = tid + 256 * j, row = c >> 4, ch = c & 15;
       v[j] = *reinterpret_cast<const u32x4*>(w_uk + ((int64_t)h * d_h + row) * d_c + c0 + 8 * ch);
     }
+    if (has_pair) rope_store(i_first, r0, r1, rpos);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int c = tid + 256 * j, row = c >> 4, ch = c & 15;
       *reinterpret_cast<LDSP u32x4*>((LDSP char*)tile + row * kAbsRowB + ch * 16) = v[j];
     }
+  }
+  for (int i = i_first + stride; i < B * half; i += stride) {   // batches beyond 256 * cblocks pairs
+    const int bb = i / half, p = i - bb * half;
+    const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
+    rope_store(i, bf16_to_f32(q_r[src]), bf16_to_f32(q_r[src + 1]), pos[bb]);
   }
   __syncthreads();
 
@@ -115,15 +144,6 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
     }
   }
 
-  // RoPE of q_r into q_abs[..., d_c:], pairs spread over the head's workgroups
-  const int half = d_R / 2;
-  for (int i = cb * 256 + tid; i < B * half; i += cblocks * 256) {
-    const int bb = i / half, p = i - bb * half;
-    const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
-    float y0, y1;
-    rope_pair(bf16_to_f32(q_r[src]), bf16_to_f32(q_r[src + 1]), pos[bb], p, d_R, base, &y0, &y1);
-    *reinterpret_cast<uint32_t*>(q_abs + ((int64_t)bb * n_h + h) * D + d_c + 2 * p) = pack_bf16(y0, y1);
-  }
 }
 
 // ---------------------------------------------------------------------------

@@ -88,14 +88,23 @@ __device__ __forceinline__ int32_t pages_of(int32_t L, int32_t bs) { return (L +
 // Block-wide page prefix over sequences.  `scan` is __shared__ scratch of
 // blockDim.x + 1 ints (blockDim.x a multiple of 64, at most 1024).  After the
 // call scan[t] = pages of sequences before thread t's chunk
-// [t*chunk, (t+1)*chunk) and scan[blockDim.x] = total P.
+// [t*chunk, (t+1)*chunk) and scan[blockDim.x] = total P.  With one sequence
+// per thread (chunk == 1) and lens_lds non-null, lens_lds[b] = seq_lens[b]
+// for every b < B, so later lookups need not go back to global memory.
 __device__ __forceinline__ void page_prefix(const int32_t* seq_lens, int32_t B, int32_t bs,
-                                            int32_t* scan, int32_t* chunk_out) {
+                                            int32_t* scan, int32_t* chunk_out,
+                                            int32_t* lens_lds = nullptr) {
   __shared__ int32_t wave_tot[16];
   const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int32_t chunk = (B + nt - 1) / nt;
   int32_t s = 0;
-  for (int32_t b = t * chunk; b < min(B, (t + 1) * chunk); ++b) s += pages_of(seq_lens[b], bs);
+  if (chunk == 1) {
+    const int32_t L = t < B ? seq_lens[t] : 0;
+    if (lens_lds && t < B) lens_lds[t] = L;
+    s = pages_of(L, bs);
+  } else {
+    for (int32_t b = t * chunk; b < min(B, (t + 1) * chunk); ++b) s += pages_of(seq_lens[b], bs);
+  }
   int32_t v = s;                         // inclusive scan inside the wave
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
@@ -120,6 +129,11 @@ __device__ __forceinline__ void locate_page(const int32_t* seq_lens, int32_t B, 
   while (hi - lo > 1) {
     int mid = (lo + hi) >> 1;
     if (scan[mid] <= x) lo = mid; else hi = mid;
+  }
+  if (chunk == 1) {                       // lo is the sequence (empty ones share its prefix)
+    *b_out = lo;
+    *first_out = scan[lo];
+    return;
   }
   int64_t first = scan[lo];
   int32_t b = lo * chunk;
