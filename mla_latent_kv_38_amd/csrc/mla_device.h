@@ -74,6 +74,14 @@ __device__ __forceinline__ void rope_pair(float x0, float x1, int32_t pos, int i
   *y1 = static_cast<float>(r1);
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations.  Direct
+// global->LDS loads (counted by vmcnt) stay in flight across it; whoever reads
+// their destination waits with an explicit vmcnt before its own barrier.
+// (__syncthreads() would also wait for every such load to land.)
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---- split-KV schedule -----------------------------------------------------
 // The batch's pages are flattened in sequence order (sequence b owns
 // ceil(L_b / block_size) consecutive pages) and cut into `parts` contiguous

@@ -8,10 +8,12 @@ namespace mla {
 // Number of compute units the launch geometry is planned for (MI355X).
 constexpr int kNumCU = 256;
 
+enum DecodeKernel { kDecodeGeneric = 0, kDecodeBf16 = 1, kDecodeFp8 = 2 };
+
 struct DecodePlan {
   int32_t parts;          // W: KV chunks the flattened page list is cut into
   int32_t head_groups;    // workgroups per part (heads split across them)
-  bool mfma;              // MFMA kernel (else the generic one)
+  DecodeKernel kernel;    // which decode kernel the dims select
   size_t ws_bytes;        // workspace needed
 };
 
@@ -40,8 +42,14 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, c
 hipError_t launch_up_v_mfma(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                             hipStream_t s, bool* handled);
 
-// Whether the MFMA decode kernel handles these dims.
+// Whether the MFMA decode kernels handle these dims (bf16 cache: 64-head
+// groups; E4M3 cache: 16-head groups).
 bool mfma_decode_supported(const mla_dims& d);
+bool fp8_decode_supported(const mla_dims& d);
+hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
+                             const void* cache, const float* kv_scale, const int32_t* block_table,
+                             int32_t max_pages, const int32_t* seq_lens, float* ws_o, float* ws_lse,
+                             void* o_lat, float* lse, hipStream_t s);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages,
