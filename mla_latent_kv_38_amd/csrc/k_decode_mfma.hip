@@ -62,7 +62,7 @@ struct DmaWalk {
   }
   __device__ __forceinline__ void issue(const char* __restrict__ src, LDSP char* dst, int k) {
     const unsigned off = static_cast<unsigned>(row * (kD * 2) + (ch == 72 ? 0 : ch * 16));
-    __builtin_amdgcn_global_load_lds(src + off, dst + 1024 * k, 16, 0, 0);
+    dma16(src, off, dst + 1024 * k);
     ch += 37;
     row += 3;
     if (ch >= 73) { ch -= 73; row += 1; }
@@ -127,13 +127,17 @@ struct Acc {                       // per-segment running state of one wave
 // no waits of its own (the explicit vmcnt + barrier at the top orders them).
 __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict__ buf,
                                           LDSP char* __restrict__ nbuf,
-                                          bool dma, const char* nsrc, const DmaWalk& walk0,
+                                          bool dma, const char* cbase, const int32_t* bt_after,
+                                          int32_t& pg_after, const DmaWalk& walk0,
                                           const bf16x8 (&qf)[36], int nvalid, float s2, Acc& acc) {
   LDSP char* pt = (LDSP char*)g_pt;
   float* xm = g_xm;
   float* xa = g_xa;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();                                               // this page landed; previous one consumed
+  asm volatile("" : "+v"(pg_after));                             // its load (one page ago) has landed
+  const char* nsrc = cbase + (int64_t)pg_after * (kBs * kD * 2); // next page
+  const int32_t pg2 = bt_after ? *bt_after : 0;                  // page id two ahead, read during this page
 
   f32x16 S = dma ? qk_page<true>(buf + ln.a_off, qf, walk0, nsrc, nbuf, ln.wave)
                  : qk_page<false>(buf + ln.a_off, qf, walk0, nsrc, nbuf, ln.wave);
@@ -149,7 +153,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   }
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
   if (ln.hi == 0) xm[ln.th * 64 + ln.hb * 32 + ln.l32] = mloc;
-  __syncthreads();                                               // page maxima exchanged
+  barrier_lds();                                                 // page maxima exchanged (next page stays in flight)
 
   const float mpage = fmaxf(mloc, xm[(1 - ln.th) * 64 + ln.hb * 32 + ln.l32]);
   float alpha = 1.f;
@@ -179,7 +183,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
       *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  __syncthreads();                                               // P^T and alpha visible
+  barrier_lds();                                                 // P^T and alpha visible
 
   // ---- PV: 16 steps (k-step ks, column block cb), one step of prefetch ------
   const float al0 = xa[ln.l32], al1 = xa[32 + ln.l32];
@@ -216,6 +220,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     vcur = vnext;
     if (cb == 3) { pc0 = pn0; pc1 = pn1; }
   }
+  pg_after = pg2;
 }
 
 __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
@@ -315,14 +320,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     acc.m_ref = -INFINITY;
     acc.l_own = 0.f;
 
+    int32_t pg_next = jp0 + 1 < jp1 ? bt[jp0 + 1] : bt[jp0];      // page ids are read one page ahead
     for (int64_t jp = jp0; jp < jp1; ++jp) {
       const bool even = ((jp - jp0) & 1) == 0;
       LDSP char* buf = even ? (LDSP char*)g_page0 : (LDSP char*)g_page1;
       LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
       const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - jp * kBs);
       const bool more = jp + 1 < jp1;
-      page_step(ln, buf, nbuf, more, cbase + (int64_t)bt[more ? jp + 1 : jp] * kPageBytesG,
-                walk0, qf, nvalid, s2, acc);
+      page_step(ln, buf, nbuf, more, cbase, jp + 2 < jp1 ? bt + jp + 2 : nullptr, pg_next, walk0, qf,
+                nvalid, s2, acc);
     }
 
     // ---- segment epilogue: normalise and store ------------------------------
@@ -383,25 +389,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 // flight at once and no LDS or barrier after the page count:
 //   o_lat = sum_k e^(lse_k - M) o_k / sum_k e^(lse_k - M),  lse = M + ln(sum).
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32_t W, int32_t HG,
-                                                   const int32_t* __restrict__ seq_lens,
-                                                   const float* __restrict__ ws_o,
-                                                   const float* __restrict__ ws_lse,
-                                                   uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
-  __shared__ int32_t scan[257];
+// One (sequence b, head group hg, wave-column block wc) of the merge.
+__device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t n_h, int32_t W, int64_t P,
+                                             int64_t np, int64_t w0, int64_t w1, const float* __restrict__ ws_o,
+                                             const float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat,
+                                             float* __restrict__ lse) {
   const int tid = threadIdx.x, lane = tid & 63, q4 = tid >> 6, l32 = lane & 31;
-  const int wc = blockIdx.x % 16, hg = (blockIdx.x / 16) % HG, b = blockIdx.x / (16 * HG);
-  if (b >= B) return;
-  int32_t chunk;
-  page_prefix(seq_lens, B, kBs, scan, &chunk);
-  const int64_t P = scan[blockDim.x];
-  int64_t pre = 0;
-  if (chunk == 1) {
-    pre = scan[b];
-  } else {
-    for (int32_t i = 0; i < b; ++i) pre += pages_of(seq_lens[i], kBs);
-  }
-  const int64_t np = pages_of(seq_lens[b], kBs);
   const int64_t head0 = (int64_t)b * n_h + (int64_t)hg * 64;
   const int col0 = 128 * (wc >> 2) + 32 * (wc & 3);
   if (np == 0) {                                   // empty sequence: zero output, lse = -inf
@@ -412,9 +405,9 @@ __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32
     if (wc == 0 && tid < 64 && lse) lse[head0 + tid] = -INFINITY;
     return;
   }
-  const int64_t w0 = part_of_page(pre, P, W), w1 = part_of_page(pre + np - 1, P, W);
   if (w0 == w1) return;                            // one part: written by the decode kernel
 
+  const bool all_live = P >= W;                    // every part holds a page unless parts outnumber pages
   const int off0 = ((wc * 2 + 0) * 4 + q4) * 256 + lane * 4;
   const int off1 = ((wc * 2 + 1) * 4 + q4) * 256 + lane * 4;
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
@@ -425,7 +418,7 @@ __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32
 #pragma unroll
     for (int jj = 0; jj < 8; ++jj) {               // part w0 always holds a page: dead parts read it
       const int64_t w = base + jj;
-      const bool live = w <= w1 && part_start(w, P, W) < part_start(w + 1, P, W);
+      const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
       const int64_t slot = (live ? w : w0) + b;
       const float* src = ws_o + (slot * n_h + (int64_t)hg * 64) * kDc;
       v0[jj] = *reinterpret_cast<const f32x4*>(src + off0);
@@ -461,6 +454,60 @@ __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32
   }
 }
 
+__global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32_t W, int32_t HG,
+                                                   const int32_t* __restrict__ seq_lens,
+                                                   const float* __restrict__ ws_o,
+                                                   const float* __restrict__ ws_lse,
+                                                   uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
+  __shared__ int32_t scan[257];
+  __shared__ int32_t w0s[256], w1s[256];           // part range of each sequence (one division per thread)
+  int32_t chunk;
+  page_prefix(seq_lens, B, kBs, scan, &chunk);
+  const int64_t P = scan[blockDim.x];
+  const int per_seq = HG * 16;
+  if (chunk == 1) {
+    {
+      const int t = threadIdx.x;
+      if (t < B && P > 0) {
+        const int64_t pre = scan[t], np = scan[t + 1] - pre;
+        w0s[t] = (int32_t)min<int64_t>(part_of_page(pre, P, W), W - 1);
+        w1s[t] = np > 0 ? (int32_t)part_of_page(pre + np - 1, P, W) : w0s[t];
+      } else if (t < B) {
+        w0s[t] = w1s[t] = 0;
+      }
+      __syncthreads();
+    }
+    // Items of the sequences whose first part ran on this workgroup's XCD
+    // (the decode kernel gives XCD x the parts [x ppx, (x+1) ppx)), so the
+    // partials are mostly read back from the L2 they were written through.
+    const int ppx = (W + 7) / 8;
+    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, J = gridDim.x >> 3;
+    auto key = [&](int32_t bb) -> int { return w0s[bb] / ppx; };
+    auto lower = [&](int x) {                      // first sequence with key >= x
+      int lo = 0, hi = B;
+      while (lo < hi) { const int mid = (lo + hi) >> 1; if (key(mid) < x) lo = mid + 1; else hi = mid; }
+      return lo;
+    };
+    const int b_lo = lower(xcd), b_hi = lower(xcd + 1);
+    const int items = (b_hi - b_lo) * per_seq;
+    for (int it = j; it < items; it += J) {
+      const int32_t b = b_lo + it / per_seq;
+      const int r = it % per_seq;
+      combine_item(b, r / 16, r % 16, n_h, W, P, scan[b + 1] - scan[b], w0s[b], w1s[b], ws_o, ws_lse, o_lat, lse);
+    }
+  } else {
+    for (int it = blockIdx.x; it < B * per_seq; it += gridDim.x) {
+      const int32_t b = it / per_seq;
+      const int r = it % per_seq;
+      int64_t pre = 0;
+      for (int32_t i = 0; i < b; ++i) pre += pages_of(seq_lens[i], kBs);
+      const int64_t np = pages_of(seq_lens[b], kBs);
+      const int64_t w0 = np > 0 ? part_of_page(pre, P, W) : 0, w1 = np > 0 ? part_of_page(pre + np - 1, P, W) : 0;
+      combine_item(b, r / 16, r % 16, n_h, W, P, np, w0, w1, ws_o, ws_lse, o_lat, lse);
+    }
+  }
+}
+
 }  // namespace
 
 bool mfma_decode_supported(const mla_dims& d) {
@@ -483,7 +530,7 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
                                        seq_lens, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, ws_o, ws_lse,
+  combine_h64<<<((B * HG * 16 + 7) / 8) * 8, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, ws_o, ws_lse,
                                           static_cast<uint16_t*>(o_lat), lse);
   return hipGetLastError();
 }

@@ -82,6 +82,24 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// Direct global -> LDS loads (LDS address = M0 + size * lane), issued from
+// inline asm so that the compiler adds no waits of its own for them: every
+// reader waits with an explicit vmcnt and a barrier.
+__device__ __forceinline__ const char* uniform(const char* p) {   // wave-uniform pointer into SGPRs
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+  return reinterpret_cast<const char*>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const char* base, uint32_t voff, const __attribute__((address_space(3))) void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(m0), "v"(voff), "s"(uniform(base)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const char* base, uint32_t voff, const __attribute__((address_space(3))) void* dst) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)));
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" :: "s"(m0), "v"(voff), "s"(uniform(base)) : "memory", "m0");
+}
+
 // ---- split-KV schedule -----------------------------------------------------
 // The batch's pages are flattened in sequence order (sequence b owns
 // ceil(L_b / block_size) consecutive pages) and cut into `parts` contiguous
