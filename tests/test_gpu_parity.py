@@ -68,6 +68,15 @@ def test_bf16_v2_shapes(lens, splits):
     _check_all(w, res)
 
 
+@pytest.mark.parametrize("splits", [200, 640])
+def test_bf16_more_parts_than_cus_and_pages(splits):
+    """More parts than CUs (several workgroup waves) and than pages (empty
+    parts inside a sequence's range, which the merge must skip)."""
+    w = W.make("v2_b16_4k", B=5, lens=[4096, 1, 700, 3000, 64], shuffle=True)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res)
+
+
 def test_empty_sequence_in_batch():
     w = W.make("v2_b16_4k", B=3, lens=[70, 0, 5])
     res = C.run_chain(w, num_splits=4)
