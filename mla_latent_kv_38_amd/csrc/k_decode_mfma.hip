@@ -71,18 +71,32 @@ struct DmaWalk {
 
 __device__ __forceinline__ int dma_count(int wave) { return wave == 0 ? 19 : 18; }
 
+// The walk is the same for every page, so each lane's 19 source offsets are
+// computed once per workgroup and kept in AGPRs (free beside the queries);
+// issuing a load then costs one register move.
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&offa)[19]) {
+  DmaWalk w;
+  w.start(wave, lane);
+#pragma unroll
+  for (int i = 0; i < 19; ++i) {
+    const uint32_t off = static_cast<uint32_t>(w.row * (kD * 2) + (w.ch == 72 ? 0 : w.ch * 16));
+    asm volatile("" : "=a"(offa[i]) : "0"(off));
+    w.ch += 37;
+    w.row += 3;
+    if (w.ch >= 73) { w.ch -= 73; w.row += 1; }
+  }
+}
+
 // S^T[32 tokens x 32 heads] = C[32 x 576] . Q^T for one wave: 36 MFMAs fed
 // from LDS four fragments ahead, Q^T read straight from AGPRs.  With kDma the
 // wave's share of the next page's direct loads is spread over the MFMAs.
 template <bool kDma>
 __device__ __forceinline__ f32x16 qk_page(const LDSP char* __restrict__ ap, const bf16x8 (&qf)[36],
-                                          const DmaWalk& walk0, const char* nsrc,
-                                          LDSP char* __restrict__ nbuf, int wave) {
+                                          const uint32_t (&offa)[19], const char* nsrc_u, uint32_t nbuf_u,
+                                          int wave) {
   f32x16 S;
 #pragma unroll
   for (int r = 0; r < 16; ++r) S[r] = 0.f;
-  DmaWalk w = walk0;
-  asm volatile("" : "+v"(w.row), "+v"(w.ch));   // keep the address walk inside the loop (no hoisting)
   constexpr int kPre = 4;
   bf16x8 af[kPre];
 #pragma unroll
@@ -91,9 +105,9 @@ __device__ __forceinline__ f32x16 qk_page(const LDSP char* __restrict__ ap, cons
   for (int kb = 0; kb < 36; ++kb) {
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(af[kb % kPre]), "a"(qf[kb]));
     if (kb + kPre < 36) af[kb % kPre] = *(const LDSP bf16x8*)(ap + 32 * (kb + kPre));
-    if (kDma && (kb & 1) == 0) w.issue(nsrc, nbuf, wave + 4 * (kb >> 1));
+    if (kDma && (kb & 1) == 0) dma16_u(nsrc_u, offa[kb >> 1], nbuf_u + 1024 * (wave + 4 * (kb >> 1)));
   }
-  if (kDma && wave == 0) w.issue(nsrc, nbuf, 4 * 18);
+  if (kDma && wave == 0) dma16_u(nsrc_u, offa[18], nbuf_u + 1024 * (4 * 18));
   asm volatile("s_nop 7\n s_nop 7\n s_nop 3" ::: "memory");       // MFMA result -> VALU
   return S;
 }
@@ -110,9 +124,10 @@ __shared__ __attribute__((aligned(16))) float g_xa[64];       // alpha per head
 __shared__ __attribute__((aligned(16))) float g_xl[2 * 64];   // row sums per token half
 __shared__ __attribute__((aligned(16))) float g_xf[64];       // final reference max
 __shared__ int32_t g_lens[256];                               // seq_lens, when the batch has <= 256
+__shared__ int32_t g_xneed[4];                                // per wave: its page half needs a new reference
 
 struct Lane {                      // per-lane constants
-  int wave, lane, l32, hi, hb, th;
+  int wave, lane, l32, hi, hb, th, hg_part;
   int a_off, pt_row, tr_off;
 };
 
@@ -128,7 +143,7 @@ struct Acc {                       // per-segment running state of one wave
 __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict__ buf,
                                           LDSP char* __restrict__ nbuf,
                                           bool dma, const char* cbase, const int32_t* bt_after,
-                                          int32_t& pg_after, const DmaWalk& walk0,
+                                          int32_t& pg_after, const uint32_t (&offa)[19],
                                           const bf16x8 (&qf)[36], int nvalid, float s2, Acc& acc) {
   LDSP char* pt = (LDSP char*)g_pt;
   float* xm = g_xm;
@@ -136,11 +151,18 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();                                               // this page landed; previous one consumed
   asm volatile("" : "+v"(pg_after));                             // its load (one page ago) has landed
-  const char* nsrc = cbase + (int64_t)pg_after * (kBs * kD * 2); // next page
+  const char* nsrc_u = uniform(cbase + (int64_t)pg_after * (kBs * kD * 2));   // next page
+  const uint32_t nbuf_u = uniform_lds(nbuf);
   const int32_t pg2 = bt_after ? *bt_after : 0;                  // page id two ahead, read during this page
 
-  f32x16 S = dma ? qk_page<true>(buf + ln.a_off, qf, walk0, nsrc, nbuf, ln.wave)
-                 : qk_page<false>(buf + ln.a_off, qf, walk0, nsrc, nbuf, ln.wave);
+  // The two head groups of a part share an L2.  Waves of matching parity
+  // (wave & 1 == head group) load their half of the next page during QK, the
+  // other half is loaded during PV, by which time the partner workgroup's
+  // early half has reached the L2: each 128-B line comes from HBM once and
+  // each CU waits for HBM latency on only half of its page.
+  const bool early = (ln.wave & 1) == ln.hg_part;
+  f32x16 S = dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
+                          : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
 
   float mloc = -INFINITY;
 #pragma unroll
@@ -153,41 +175,55 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   }
   mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
   if (ln.hi == 0) xm[ln.th * 64 + ln.hb * 32 + ln.l32] = mloc;
-  barrier_lds();                                                 // page maxima exchanged (next page stays in flight)
-
-  const float mpage = fmaxf(mloc, xm[(1 - ln.th) * 64 + ln.hb * 32 + ln.l32]);
-  float alpha = 1.f;
-  if (mpage > acc.m_ref + kTau) {
-    alpha = __builtin_amdgcn_exp2f(acc.m_ref - mpage);
-    acc.m_ref = mpage;
-  }
+  // Optimistic P: computed with the current reference maximum.  Only if some
+  // token half of the page exceeds it by more than 2^tau (always on a
+  // segment's first page, rarely after) do all waves redo P below with the
+  // page maximum, exactly as the lazy rule prescribes; the common page thus
+  // needs one barrier between QK and PV instead of two.
+  const int need = __any(mloc > acc.m_ref + kTau);
+  if (ln.lane == 0) g_xneed[ln.wave] = need;
   float ps = 0.f;
-  uint32_t pk[8];
+  auto make_p = [&]() {
+    uint32_t pk[8];
+    ps = 0.f;
 #pragma unroll
-  for (int r = 0; r < 16; r += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(S[r] - acc.m_ref);
-    const float p1 = __builtin_amdgcn_exp2f(S[r + 1] - acc.m_ref);
-    ps += p0 + p1;
-    pk[r >> 1] = pack_bf16(p0, p1);
-  }
-  acc.l_own = acc.l_own * alpha + ps;
-  if (ln.th == 0 && ln.hi == 0) xa[ln.hb * 32 + ln.l32] = alpha;
+    for (int r = 0; r < 16; r += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(S[r] - acc.m_ref);
+      const float p1 = __builtin_amdgcn_exp2f(S[r + 1] - acc.m_ref);
+      ps += p0 + p1;
+      pk[r >> 1] = pack_bf16(p0, p1);
+    }
 #pragma unroll
-  for (int ra = 0; ra < 4; ++ra) {
-    const int slot = 16 * (2 * ln.th + (ra >> 1)) + 4 * (2 * (ra & 1) + ln.hi);
-    *(LDSP u32x2*)(pt + ln.pt_row + slot * 2) = u32x2{pk[2 * ra], pk[2 * ra + 1]};
-  }
+    for (int ra = 0; ra < 4; ++ra) {
+      const int slot = 16 * (2 * ln.th + (ra >> 1)) + 4 * (2 * (ra & 1) + ln.hi);
+      *(LDSP u32x2*)(pt + ln.pt_row + slot * 2) = u32x2{pk[2 * ra], pk[2 * ra + 1]};
+    }
+  };
+  make_p();
   if (nvalid < kBs) {                                            // rows past the end: zero the latent
     for (int i = threadIdx.x; i < (kBs - nvalid) * 64; i += 256) {
       const int row = nvalid + (i >> 6), ch = i & 63;
       *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   }
-  barrier_lds();                                                 // P^T and alpha visible
+  barrier_lds();                                                 // P^T, page maxima and flags visible
+  const bool slow = (g_xneed[0] | g_xneed[1] | g_xneed[2] | g_xneed[3]) != 0;
+  float alpha = 1.f;
+  if (slow) {
+    const float mpage = fmaxf(mloc, xm[(1 - ln.th) * 64 + ln.hb * 32 + ln.l32]);
+    if (mpage > acc.m_ref + kTau) {
+      alpha = __builtin_amdgcn_exp2f(acc.m_ref - mpage);
+      acc.m_ref = mpage;
+    }
+    make_p();
+    if (ln.th == 0 && ln.hi == 0) xa[ln.hb * 32 + ln.l32] = alpha;
+    barrier_lds();                                               // P^T and alpha visible
+  }
+  acc.l_own = acc.l_own * alpha + ps;
 
   // ---- PV: 16 steps (k-step ks, column block cb), one step of prefetch ------
-  const float al0 = xa[ln.l32], al1 = xa[32 + ln.l32];
-  if (__any(al0 != 1.f || al1 != 1.f)) {
+  const float al0 = slow ? xa[ln.l32] : 1.f, al1 = slow ? xa[32 + ln.l32] : 1.f;
+  if (slow && __any(al0 != 1.f || al1 != 1.f)) {
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
@@ -217,8 +253,14 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n"
                  "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
                  : "+v"(acc.o[cb][0]), "+v"(acc.o[cb][1]) : "v"(vcur), "v"(pc0), "v"(pc1));
+    if (dma && !early) dma16_u(nsrc_u, offa[step], nbuf_u + 1024 * (ln.wave + 4 * step));
     vcur = vnext;
     if (cb == 3) { pc0 = pn0; pc1 = pn1; }
+  }
+  if (dma && !early) {
+    dma16_u(nsrc_u, offa[16], nbuf_u + 1024 * (ln.wave + 64));
+    dma16_u(nsrc_u, offa[17], nbuf_u + 1024 * (ln.wave + 68));
+    if (ln.wave == 0) dma16_u(nsrc_u, offa[18], nbuf_u + 1024 * 72);
   }
   pg_after = pg2;
 }
@@ -245,6 +287,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   const int ppx = (W + 7) / 8;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int hg = j % HG;
+  ln.hg_part = hg & 1;
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
@@ -273,8 +316,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     ln.tr_off = (4 * (sg >> 2) + 2 * ln.hi) * kRowB + (128 * ln.wave + 16 * (g & 1) + 4 * (sg & 3)) * 2;
   }
 
-  DmaWalk walk0;
-  walk0.start(ln.wave, ln.lane);
+  uint32_t offa[19];                                             // this lane's page-load offsets (AGPRs)
+  dma_offsets(ln.wave, ln.lane, offa);
   const int ndma = dma_count(ln.wave);
   const char* cbase = reinterpret_cast<const char*>(cache);
   constexpr int64_t kPageBytesG = (int64_t)kBs * kD * 2;
@@ -289,12 +332,18 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
     // 1, both as whole 1 KiB direct loads.
-    {
-      DmaWalk w = walk0, wq = walk0;
-      const char* src = cbase + (int64_t)bt[jp0] * kPageBytesG;
-      const char* qsrc = reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD);
-      for (int i = 0; i < ndma; ++i) w.issue(src, (LDSP char*)g_page0, ln.wave + 4 * i);
-      for (int i = 0; i < ndma; ++i) wq.issue(qsrc, (LDSP char*)g_page1, ln.wave + 4 * i);
+    {                                                            // queries first: they need no page id
+      const char* qsrc_u = uniform(reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD));
+      const uint32_t q_m0 = uniform_lds((LDSP char*)g_page1);
+#pragma unroll
+      for (int i = 0; i < 19; ++i)
+        if (i < ndma) dma16_u(qsrc_u, offa[i], q_m0 + 1024 * (ln.wave + 4 * i));
+      const int32_t pg0 = sload_i32(bt + jp0);
+      const char* src_u = uniform(cbase + (int64_t)pg0 * kPageBytesG);
+      const uint32_t p_m0 = uniform_lds((LDSP char*)g_page0);
+#pragma unroll
+      for (int i = 0; i < 19; ++i)
+        if (i < ndma) dma16_u(src_u, offa[i], p_m0 + 1024 * (ln.wave + 4 * i));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
@@ -327,7 +376,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
       const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - jp * kBs);
       const bool more = jp + 1 < jp1;
-      page_step(ln, buf, nbuf, more, cbase, jp + 2 < jp1 ? bt + jp + 2 : nullptr, pg_next, walk0, qf,
+      page_step(ln, buf, nbuf, more, cbase, jp + 2 < jp1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
                 nvalid, s2, acc);
     }
 

@@ -100,6 +100,24 @@ __device__ __forceinline__ void dma4(const char* base, uint32_t voff, const __at
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" :: "s"(m0), "v"(voff), "s"(uniform(base)) : "memory", "m0");
 }
 
+// The same with a source base and an LDS address the caller has already made
+// wave-uniform (SGPRs), so each load costs no extra scalar moves.
+__device__ __forceinline__ void dma16_u(const char* ubase, uint32_t voff, uint32_t um0) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" :: "s"(um0), "v"(voff), "s"(ubase) : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t uniform_lds(const __attribute__((address_space(3))) void* p) {
+  return __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(reinterpret_cast<uintptr_t>(p)));
+}
+
+// Scalar load of one int32 at a wave-uniform address; waits for itself (the
+// wait covers only scalar and LDS operations, never the vector loads in flight).
+__device__ __forceinline__ int32_t sload_i32(const int32_t* p) {
+  int32_t v;
+  const char* u = uniform(reinterpret_cast<const char*>(p));
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(u) : "memory");
+  return v;
+}
+
 // ---- split-KV schedule -----------------------------------------------------
 // The batch's pages are flattened in sequence order (sequence b owns
 // ceil(L_b / block_size) consecutive pages) and cut into `parts` contiguous
