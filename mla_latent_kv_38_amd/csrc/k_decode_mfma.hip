@@ -44,9 +44,6 @@ constexpr int kPageB = kBs * kRowB;         // 74752 = 73 x 1 KiB
 constexpr int kPtRowB = 144;                // P^T row: 64 bf16 + 16 pad
 constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
 
 // Copy one 64-token page (64 x 1152 B) into the padded LDS tile: 73 direct
 // loads of 64 lanes x 16 B; LDS slot s = 64 k + lane holds row s / 73, 16-B
@@ -164,16 +161,20 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   f32x16 S = dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
                           : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
 
-  float mloc = -INFINITY;
+  // Scores stay raw (s2 > 0 commutes with the maximum); rows past the end of
+  // the sequence are -inf.  P below is exp2(S s2 - m) in one fma per score.
+  if (nvalid < kBs) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int ra = r >> 2;
-    const int t = 32 * ln.th + 16 * (ra >> 1) + 2 * (ra & 1) + ln.hi + 4 * (r & 3);
-    const float v = t < nvalid ? S[r] * s2 : -INFINITY;
-    S[r] = v;
-    mloc = fmaxf(mloc, v);
+    for (int r = 0; r < 16; ++r) {
+      const int ra = r >> 2;
+      const int t = 32 * ln.th + 16 * (ra >> 1) + 2 * (ra & 1) + ln.hi + 4 * (r & 3);
+      if (t >= nvalid) S[r] = -INFINITY;
+    }
   }
-  mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+  float mloc = fmaxf(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])), fmaxf(fmaxf(S[4], S[5]), fmaxf(S[6], S[7])));
+  mloc = fmaxf(mloc, fmaxf(fmaxf(fmaxf(S[8], S[9]), fmaxf(S[10], S[11])),
+                           fmaxf(fmaxf(S[12], S[13]), fmaxf(S[14], S[15]))));
+  mloc = max_xor32(mloc) * s2;
   if (ln.hi == 0) xm[ln.th * 64 + ln.hb * 32 + ln.l32] = mloc;
   // Optimistic P: computed with the current reference maximum.  Only if some
   // token half of the page exceeds it by more than 2^tau (always on a
@@ -188,10 +189,10 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(S[r] - acc.m_ref);
-      const float p1 = __builtin_amdgcn_exp2f(S[r + 1] - acc.m_ref);
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], s2, -acc.m_ref));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], s2, -acc.m_ref));
       ps += p0 + p1;
-      pk[r >> 1] = pack_bf16(p0, p1);
+      pk[r >> 1] = pack2_bf16(p0, p1);
     }
 #pragma unroll
     for (int ra = 0; ra < 4; ++ra) {
@@ -383,7 +384,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     // ---- segment epilogue: normalise and store ------------------------------
     asm volatile("s_nop 7\n s_nop 7\n s_nop 3" ::: "memory");   // MFMA result -> VALU
     __syncthreads();
-    const float l_lane = acc.l_own + __shfl_xor(acc.l_own, 32);
+    const float l_lane = sum_xor32(acc.l_own);
     if (ln.hi == 0) {
       g_xl[ln.th * 64 + ln.hb * 32 + ln.l32] = l_lane;
       if (ln.th == 0) g_xf[ln.hb * 32 + ln.l32] = acc.m_ref;
@@ -406,7 +407,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
           const float o2 = acc.o[cb][h2][4 * q4 + 2] * inv, o3 = acc.o[cb][h2][4 * q4 + 3] * inv;
           if (whole) {
             *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
-                u32x2{pack_bf16(o0, o1), pack_bf16(o2, o3)};
+                u32x2{pack2_bf16(o0, o1), pack2_bf16(o2, o3)};
           } else {                                               // quad ((w*4+cb)*2+h2)*4+q4: 64 lanes x 16 B
             const int quad = ((ln.wave * 4 + cb) * 2 + h2) * 4 + q4;
             *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + (int64_t)hg * 64) * kDc +
@@ -494,9 +495,9 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
   const int col = col0 + 8 * q4 + 4 * (lane >> 5);
   const float i0 = 1.f / d0, i1 = 1.f / d1;
   *reinterpret_cast<u32x2*>(o_lat + (head0 + l32) * kDc + col) =
-      u32x2{pack_bf16(acc0[0] * i0, acc0[1] * i0), pack_bf16(acc0[2] * i0, acc0[3] * i0)};
+      u32x2{pack2_bf16(acc0[0] * i0, acc0[1] * i0), pack2_bf16(acc0[2] * i0, acc0[3] * i0)};
   *reinterpret_cast<u32x2*>(o_lat + (head0 + 32 + l32) * kDc + col) =
-      u32x2{pack_bf16(acc1[0] * i1, acc1[1] * i1), pack_bf16(acc1[2] * i1, acc1[3] * i1)};
+      u32x2{pack2_bf16(acc1[0] * i1, acc1[1] * i1), pack2_bf16(acc1[2] * i1, acc1[3] * i1)};
   if (wc == 0 && tid < 32 && lse) {
     lse[head0 + l32] = m0 + __logf(d0);
     lse[head0 + 32 + l32] = m1 + __logf(d1);

@@ -20,6 +20,35 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return static_cast<uint16_t>(u >> 16);
 }
 
+// Two floats -> packed bfloat16 pair (low half = a), round to nearest even,
+// by the hardware conversion (one instruction).
+typedef __bf16 mla_bf16x2 __attribute__((ext_vector_type(2)));
+typedef float mla_f32x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((mla_f32x2){a, b}, mla_bf16x2));
+}
+
+// Reductions across lanes l, l ^ 32 (and l ^ 16) of a wave without going
+// through LDS: the lane-swap instructions exchange the 32-lane halves (the
+// odd and even 16-lane rows) of two registers; with both operands equal, the
+// two results hold each lane's value and its partner's.
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // E4M3 (OCP): exponent bias 7, 3 mantissa bits, subnormals m * 2^-9, max 448.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   uint32_t s = (c >> 7) & 1u, e = (c >> 3) & 0xFu, m = c & 7u;
