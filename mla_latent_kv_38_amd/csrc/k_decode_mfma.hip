@@ -391,33 +391,47 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     }
     __syncthreads();
     const bool whole = (jp0 == 0 && jp1 == np);
+    float inv[2];
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       const int hh = h2 * 32 + ln.l32;
       const float lt = g_xl[hh] + g_xl[64 + hh];
-      const float inv = 1.f / lt;
+      inv[h2] = 1.f / lt;
       const float lse_v = (g_xf[hh] + __log2f(lt)) * 0.69314718055994531f;
       const int64_t head = (int64_t)hg * 64 + hh;
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int col = 128 * ln.wave + 32 * cb + 8 * q4 + 4 * ln.hi;
-          const float o0 = acc.o[cb][h2][4 * q4] * inv, o1 = acc.o[cb][h2][4 * q4 + 1] * inv;
-          const float o2 = acc.o[cb][h2][4 * q4 + 2] * inv, o3 = acc.o[cb][h2][4 * q4 + 3] * inv;
-          if (whole) {
-            *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
-                u32x2{pack2_bf16(o0, o1), pack2_bf16(o2, o3)};
-          } else {                                               // quad ((w*4+cb)*2+h2)*4+q4: 64 lanes x 16 B
-            const int quad = ((ln.wave * 4 + cb) * 2 + h2) * 4 + q4;
-            *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + (int64_t)hg * 64) * kDc +
-                                      quad * 256 + ln.lane * 4) = f32x4{o0, o1, o2, o3};
-          }
-        }
       if (ln.wave == 0 && ln.hi == 0) {
         if (whole) { if (lse) lse[(int64_t)b * n_h + head] = lse_v; }
         else ws_lse[((int64_t)part + b) * n_h + head] = lse_v;
       }
+    }
+    if (whole) {
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int col = 128 * ln.wave + 32 * cb + 8 * q4 + 4 * ln.hi;
+            const f32x16& o = acc.o[cb][h2];
+            *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + (int64_t)hg * 64 + h2 * 32 + ln.l32) * kDc + col) =
+                u32x2{pack2_bf16(o[4 * q4] * inv[h2], o[4 * q4 + 1] * inv[h2]),
+                      pack2_bf16(o[4 * q4 + 2] * inv[h2], o[4 * q4 + 3] * inv[h2])};
+          }
+    } else {                                                     // bf16 partial, quad (w*4+cb)*4+q4: 64 lanes x 16 B
+      uint16_t* wp = reinterpret_cast<uint16_t*>(ws_o) + (((int64_t)part + b) * n_h + (int64_t)hg * 64) * kDc +
+                     ln.lane * 8;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x16& o0 = acc.o[cb][0];
+          const f32x16& o1 = acc.o[cb][1];
+          *reinterpret_cast<u32x4*>(wp + ((ln.wave * 4 + cb) * 4 + q4) * 512) =
+              u32x4{pack2_bf16(o0[4 * q4] * inv[0], o0[4 * q4 + 1] * inv[0]),
+                    pack2_bf16(o0[4 * q4 + 2] * inv[0], o0[4 * q4 + 3] * inv[0]),
+                    pack2_bf16(o1[4 * q4] * inv[1], o1[4 * q4 + 1] * inv[1]),
+                    pack2_bf16(o1[4 * q4 + 2] * inv[1], o1[4 * q4 + 3] * inv[1])};
+        }
     }
 
     x += jp1 - jp0;
@@ -430,11 +444,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 
 // ---------------------------------------------------------------------------
 // Merge of the split-KV partials of decode_mfma_h64.  A partial (slot, 64-head
-// group) is 128 KiB in register order: quad ((w*4 + cb)*2 + h2)*4 + q4 holds,
-// for lane l, latent columns 128w + 32cb + 8q4 + 4(l/32) .. +3 of head
-// 32h2 + l%32, already divided by its own row sum; its log-sum-exp is in
-// ws_lse.  Workgroup = (sequence, head group, wave-column block w*4+cb);
-// thread (q4, l) owns two float4 of each partial (h2 = 0, 1).  Parts are
+// group) is 64 KiB of bfloat16 in register order: quad (w*4 + cb)*4 + q4
+// holds, for lane l, 16 B: latent columns 128w + 32cb + 8q4 + 4(l/32) .. +3
+// of head l%32, then the same columns of head 32 + l%32, already divided by
+// the partial's own row sum; its log-sum-exp (float32) is in ws_lse.
+// Workgroup = (sequence, head group, wave-column block w*4+cb); thread
+// (q4, l) owns one 16-B chunk of each partial.  Parts are
 // merged eight at a time with a running maximum, every load of a batch in
 // flight at once and no LDS or barrier after the page count:
 //   o_lat = sum_k e^(lse_k - M) o_k / sum_k e^(lse_k - M),  lse = M + ln(sum).
@@ -458,8 +473,8 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
   if (w0 == w1) return;                            // one part: written by the decode kernel
 
   const bool all_live = P >= W;                    // every part holds a page unless parts outnumber pages
-  const int off0 = ((wc * 2 + 0) * 4 + q4) * 256 + lane * 4;
-  const int off1 = ((wc * 2 + 1) * 4 + q4) * 256 + lane * 4;
+  const int off = (wc * 4 + q4) * 512 + lane * 8;
+  const uint16_t* ws16 = reinterpret_cast<const uint16_t*>(ws_o);
   f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   float m0 = -INFINITY, m1 = -INFINITY, d0 = 0.f, d1 = 0.f;
   for (int64_t base = w0; base <= w1; base += 8) {
@@ -470,9 +485,11 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
       const int64_t w = base + jj;
       const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
       const int64_t slot = (live ? w : w0) + b;
-      const float* src = ws_o + (slot * n_h + (int64_t)hg * 64) * kDc;
-      v0[jj] = *reinterpret_cast<const f32x4*>(src + off0);
-      v1[jj] = *reinterpret_cast<const f32x4*>(src + off1);
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(ws16 + (slot * n_h + (int64_t)hg * 64) * kDc + off);
+      v0[jj] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+      v1[jj] = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
+                     __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
       const float* ls = ws_lse + slot * n_h + (int64_t)hg * 64;
       e0[jj] = live ? ls[l32] : -INFINITY;
       e1[jj] = live ? ls[32 + l32] : -INFINITY;
