@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--min-replica-mb", type=float, default=600.0)
     p.add_argument("--cpu-sample-seqs", type=int, default=2)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="replay each step from a captured HIP graph (one graph per cache replica)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against known bytes)")
@@ -156,7 +158,7 @@ def main():
 
     def step(i, ev=None):
         rp = reps[i % R]
-        rec = (lambda k: ev[k].record(stream)) if ev is not None else (lambda k: None)
+        rec = (lambda k: ev[k].record(stream) if ev[k] is not None else None) if ev is not None else (lambda k: None)
         rec(0)
         mla.absorb_q(d, q_c, q_r, q_pos, rp["w_uk"], q_abs)
         rec(1)
@@ -171,21 +173,47 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    graphs = None
+    if args.graph:
+        # the library allocates nothing and issues no memset, so a step captures
+        # as four kernel launches (five with the split-KV merge) per replica
+        graphs = []
+        for r in range(R):
+            gph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gph):
+                step(r)
+            graphs.append(gph)
+        for i in range(args.warmup):
+            graphs[i % R].replay()
+        torch.cuda.synchronize()
 
-    # timed region: K whole steps
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: K whole steps; events only around the decode call (the
+    # roofline kernel), on the stream the library launches on
+    new_ev = lambda: torch.cuda.Event(enable_timing=True)
+    t0, t1 = new_ev(), new_ev()
+    dec_evs = [[None, None, new_ev(), new_ev(), None] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            step(i, dec_evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
     ms_step = ms_total / args.steps
+    dec_us = None if graphs is not None else float(np.mean([e[2].elapsed_time(e[3]) for e in dec_evs]) * 1e3)
+
+    # per-call breakdown: a second, untimed pass with an event between calls
+    evs = [[new_ev() for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
     call_us = {name: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
                for k, name in enumerate(["absorb_q", "cache_append", "decode", "up_v"])}
-    dec_us = call_us["decode"]
+    if dec_us is None:                   # graph replay: the decode call is timed in the eager pass
+        dec_us = call_us["decode"]
 
     # algorithmic work of one decode call
     toks = int(w.lens.sum())
@@ -220,7 +248,8 @@ def main():
         "config": {"workload": args.workload, "batch": B, "seq_len": int(w.lens.max()),
                    "total_tokens": toks, "n_heads": nh, "d_head": w.d_h, "d_latent": w.d_c,
                    "d_rope": w.d_R, "block_size": w.block_size, "kv_dtype": w.kv,
-                   "replicas": R, "num_splits": args.splits},
+                   "replicas": R, "num_splits": args.splits,
+                   "launch": "graph" if graphs is not None else "eager"},
         "steps_per_s": round(1e3 / ms_step, 1),
         "step_tflops": round(dec_flops / (ms_step * 1e-3) / 1e12, 1),
         "decode_us": round(dec_us, 3),
