@@ -1,6 +1,8 @@
 // Generic kernels: any head/latent/RoPE widths, float32 or bfloat16 activations,
 // float32 / bfloat16 / E4M3 cache.  Plain FMA arithmetic; the MFMA decode path
 // for DeepSeek-V2 shapes lives in k_decode_mfma.hip.
+#include <cmath>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -22,7 +24,7 @@ __global__ void __launch_bounds__(256) absorb_q_generic(int32_t B, int32_t n_h, 
                                                         const T* __restrict__ q_r,
                                                         const int32_t* __restrict__ pos,
                                                         const T* __restrict__ w_uk,
-                                                        T* __restrict__ q_abs, double base) {
+                                                        T* __restrict__ q_abs, double log2_base) {
   extern __shared__ float sq[];  // [kBB][d_h]
   const int h = blockIdx.x;
   const int c = blockIdx.y * blockDim.x + threadIdx.x;
@@ -53,7 +55,7 @@ __global__ void __launch_bounds__(256) absorb_q_generic(int32_t B, int32_t n_h, 
       int bb = i / half, p = i % half;
       int64_t src = ((int64_t)(b0 + bb) * n_h + h) * d_R + 2 * p;
       float y0, y1;
-      rope_pair(io<T>::load(q_r, src), io<T>::load(q_r, src + 1), pos[b0 + bb], p, d_R, base, &y0, &y1);
+      rope_pair(io<T>::load(q_r, src), io<T>::load(q_r, src + 1), pos[b0 + bb], p, d_R, log2_base, &y0, &y1);
       int64_t dst = ((int64_t)(b0 + bb) * n_h + h) * D + d_c + 2 * p;
       io<T>::store(q_abs, dst, y0);
       io<T>::store(q_abs, dst + 1, y1);
@@ -75,7 +77,7 @@ __global__ void __launch_bounds__(64) cache_append_generic(int32_t d_c, int32_t 
                                                            const int64_t* __restrict__ slot,
                                                            void* __restrict__ cache,
                                                            float* __restrict__ kv_scale,
-                                                           double base) {
+                                                           double log2_base) {
   const int t = blockIdx.x, lane = threadIdx.x;
   const int D = d_c + d_R;
   const int64_t s = slot[t];
@@ -90,7 +92,7 @@ __global__ void __launch_bounds__(64) cache_append_generic(int32_t d_c, int32_t 
       int r = e - d_c, pr = r >> 1;
       float y0, y1;
       rope_pair(io<T>::load(k_r, (int64_t)t * d_R + 2 * pr), io<T>::load(k_r, (int64_t)t * d_R + 2 * pr + 1),
-                p, pr, d_R, base, &y0, &y1);
+                p, pr, d_R, log2_base, &y0, &y1);
       x = (r & 1) ? y1 : y0;
     }
     v[n] = x;
@@ -356,10 +358,10 @@ hipError_t launch_absorb_q(const mla_dims& d, int32_t B, const void* q_c, const 
   size_t shm = sizeof(float) * kBB * d.d_head;
   if (d.act_dtype == MLA_F32)
     absorb_q_generic<float><<<grid, 256, shm, s>>>(B, d.n_heads, d.d_head, d.d_latent, d.d_rope,
-        (const float*)q_c, (const float*)q_r, pos, (const float*)w_uk, (float*)q_abs, d.rope_base);
+        (const float*)q_c, (const float*)q_r, pos, (const float*)w_uk, (float*)q_abs, std::log2(d.rope_base));
   else
     absorb_q_generic<bf16_t><<<grid, 256, shm, s>>>(B, d.n_heads, d.d_head, d.d_latent, d.d_rope,
-        (const bf16_t*)q_c, (const bf16_t*)q_r, pos, (const bf16_t*)w_uk, (bf16_t*)q_abs, d.rope_base);
+        (const bf16_t*)q_c, (const bf16_t*)q_r, pos, (const bf16_t*)w_uk, (bf16_t*)q_abs, std::log2(d.rope_base));
   return hipGetLastError();
 }
 
@@ -370,11 +372,11 @@ static void append_dispatch(const mla_dims& d, int32_t T_, const void* c_kv, con
   const T* c = static_cast<const T*>(c_kv);
   const T* k = static_cast<const T*>(k_r);
   if (d.kv_dtype == MLA_F32)
-    cache_append_generic<T, MLA_F32><<<T_, 64, 0, s>>>(d.d_latent, d.d_rope, c, k, pos, slot, cache, kv_scale, d.rope_base);
+    cache_append_generic<T, MLA_F32><<<T_, 64, 0, s>>>(d.d_latent, d.d_rope, c, k, pos, slot, cache, kv_scale, std::log2(d.rope_base));
   else if (d.kv_dtype == MLA_BF16)
-    cache_append_generic<T, MLA_BF16><<<T_, 64, 0, s>>>(d.d_latent, d.d_rope, c, k, pos, slot, cache, kv_scale, d.rope_base);
+    cache_append_generic<T, MLA_BF16><<<T_, 64, 0, s>>>(d.d_latent, d.d_rope, c, k, pos, slot, cache, kv_scale, std::log2(d.rope_base));
   else
-    cache_append_generic<T, MLA_E4M3><<<T_, 64, 0, s>>>(d.d_latent, d.d_rope, c, k, pos, slot, cache, kv_scale, d.rope_base);
+    cache_append_generic<T, MLA_E4M3><<<T_, 64, 0, s>>>(d.d_latent, d.d_rope, c, k, pos, slot, cache, kv_scale, std::log2(d.rope_base));
 }
 
 hipError_t launch_cache_append(const mla_dims& d, int32_t T_, const void* c_kv, const void* k_r,

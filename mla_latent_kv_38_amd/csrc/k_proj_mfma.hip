@@ -11,6 +11,8 @@
 //
 // 16x16x32 operand layouts (lane l, group g = l / 16, s = l % 16):
 //   A: A[s][8g + e], e = 0..7      B: B[8g + e][s]      D: D[4g + r][s], r = 0..3
+#include <cmath>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -49,7 +51,7 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
                                                      const uint16_t* __restrict__ q_r,
                                                      const int32_t* __restrict__ pos,
                                                      const uint16_t* __restrict__ w_uk,
-                                                     uint16_t* __restrict__ q_abs, double base) {
+                                                     uint16_t* __restrict__ q_abs, double log2_base) {
   constexpr int d_h = 32 * kKs;
   __shared__ __attribute__((aligned(16))) char tile[d_h * kAbsRowB];
   const int cblocks = d_c / kAbsCols;
@@ -78,7 +80,7 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
   auto rope_store = [&](int i, float x0, float x1, int32_t ps) {
     const int bb = i / half, p = i - bb * half;
     float y0, y1;
-    rope_pair(x0, x1, ps, p, d_R, base, &y0, &y1);
+    rope_pair(x0, x1, ps, p, d_R, log2_base, &y0, &y1);
     *reinterpret_cast<uint32_t*>(q_abs + ((int64_t)bb * n_h + h) * D + d_c + 2 * p) = pack_bf16(y0, y1);
   };
 
@@ -223,10 +225,10 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, c
   auto w = static_cast<const uint16_t*>(w_uk);
   auto qa = static_cast<uint16_t*>(q_abs);
   switch (d.d_head) {
-    case 64:  absorb_q_mfma<2><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, d.rope_base); break;
-    case 128: absorb_q_mfma<4><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, d.rope_base); break;
-    case 192: absorb_q_mfma<6><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, d.rope_base); break;
-    case 256: absorb_q_mfma<8><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, d.rope_base); break;
+    case 64:  absorb_q_mfma<2><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 128: absorb_q_mfma<4><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 192: absorb_q_mfma<6><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 256: absorb_q_mfma<8><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
     default: return hipSuccess;
   }
   *handled = true;

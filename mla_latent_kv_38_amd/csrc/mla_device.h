@@ -88,17 +88,20 @@ template <> struct io<bf16_t> {
 };
 
 // RoPE of one pair (x0, x1) at position pos, frequency index i of d_rope/2:
-// angle = pos * base^(-2i/d_rope); rotation in float64 without contraction,
-// result rounded to float32.
+// angle = pos * base^(-2i/d_rope), with the frequency formed as
+// 2^(-(2i/d_rope) log2(base)) (the caller passes log2(base), computed once on
+// the host); angle, sine, cosine and rotation in float64 without
+// contraction, result rounded to float32.
 __device__ __forceinline__ void rope_pair(float x0, float x1, int32_t pos, int i, int d_rope,
-                                          double base, float* y0, float* y1) {
+                                          double log2_base, float* y0, float* y1) {
 #pragma clang fp contract(off)
-  double inv = pow(base, -2.0 * static_cast<double>(i) / static_cast<double>(d_rope));
-  double ang = static_cast<double>(pos) * inv;
-  double c = cos(ang), s = sin(ang);
-  double a = static_cast<double>(x0), b = static_cast<double>(x1);
-  double r0 = a * c - b * s;
-  double r1 = a * s + b * c;
+  const double inv = exp2(-(2.0 * static_cast<double>(i) / static_cast<double>(d_rope)) * log2_base);
+  const double ang = static_cast<double>(pos) * inv;
+  double s, c;
+  sincos(ang, &s, &c);
+  const double a = static_cast<double>(x0), b = static_cast<double>(x1);
+  const double r0 = a * c - b * s;
+  const double r1 = a * s + b * c;
   *y0 = static_cast<float>(r0);
   *y1 = static_cast<float>(r1);
 }
