@@ -84,6 +84,20 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
     *reinterpret_cast<uint32_t*>(q_abs + ((int64_t)bb * n_h + h) * D + d_c + 2 * p) = pack_bf16(y0, y1);
   };
 
+  // q_C rows of the first batch block, in flight together with the weight tile
+  auto load_q = [&](int b0, bf16x8 (&qf)[kKs]) {
+    const int b = b0 + s;
+#pragma unroll
+    for (int ks = 0; ks < kKs; ++ks) {
+      if (b < B)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(q_c + ((int64_t)b * n_h + h) * d_h + 32 * ks + 8 * g);
+      else
+        qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    }
+  };
+  bf16x8 qf[kKs];
+  load_q(0, qf);
+
   // stage W_UK[h][:, c0:c0+128] (d_h rows of 256 B): all loads first, then the LDS writes
   {
     constexpr int kPer = d_h * 16 / 256;
@@ -125,14 +139,7 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
 
   for (int b0 = 0; b0 < B; b0 += 16) {
     const int b = b0 + s;
-    bf16x8 qf[kKs];
-#pragma unroll
-    for (int ks = 0; ks < kKs; ++ks) {
-      if (b < B)
-        qf[ks] = *reinterpret_cast<const bf16x8*>(q_c + ((int64_t)b * n_h + h) * d_h + 32 * ks + 8 * g);
-      else
-        qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
-    }
+    if (b0 > 0) load_q(b0, qf);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
