@@ -216,18 +216,14 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
-  int32_t* scan = reinterpret_cast<int32_t*>(g_tile);
-  int32_t chunk;
-  page_prefix(seq_lens, B, kBs, scan, &chunk, g_lens);
+  const PartRange pr = locate_part(seq_lens, B, kBs, part, W, g_lens);
+  const int32_t chunk = pr.chunk;
   auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
-  const int64_t P = scan[blockDim.x];
-  const int64_t x1 = part_start(part + 1, P, W);
-  int64_t x = part_start(part, P, W);
+  const int64_t x1 = pr.x1;
+  int64_t x = pr.x0;
   if (x >= x1) return;
-  int32_t b;
-  int64_t first;
-  locate_page(seq_lens, B, kBs, scan, chunk, x, &b, &first);
-  __syncthreads();                                              // scan (in the tile) no longer read
+  int32_t b = pr.b;
+  int64_t first = pr.first;
 
   const char* cbase = reinterpret_cast<const char*>(cache);
   for (;;) {

@@ -292,18 +292,14 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
-  int32_t* scan = reinterpret_cast<int32_t*>(g_pt);
-  int32_t chunk;
-  page_prefix(seq_lens, B, kBs, scan, &chunk, g_lens);
+  const PartRange pr = locate_part(seq_lens, B, kBs, part, W, g_lens);
+  const int32_t chunk = pr.chunk;
   auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
-  const int64_t P = scan[blockDim.x];
-  const int64_t x1 = part_start(part + 1, P, W);
-  int64_t x = part_start(part, P, W);
+  const int64_t x1 = pr.x1;
+  int64_t x = pr.x0;
   if (x >= x1) return;
-  int32_t b;
-  int64_t first;
-  locate_page(seq_lens, B, kBs, scan, chunk, x, &b, &first);
-  __syncthreads();
+  int32_t b = pr.b;
+  int64_t first = pr.first;
 
   // QK A operand: lane reads token row tok(l32) of its half, 16-B chunk hi of each k-step
   {
@@ -333,21 +329,37 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
     // 1, both as whole 1 KiB direct loads.
+    int32_t pg0, pg_next;
+    Acc acc;                                                     // cleared while the first loads are in flight
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc.o[cb][h2][r] = 0.f;
+    acc.m_ref = -INFINITY;
+    acc.l_own = 0.f;
     {                                                            // queries first: they need no page id
       const char* qsrc_u = uniform(reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD));
       const uint32_t q_m0 = uniform_lds((LDSP char*)g_page1);
 #pragma unroll
       for (int i = 0; i < 19; ++i)
         if (i < ndma) dma16_u(qsrc_u, offa[i], q_m0 + 1024 * (ln.wave + 4 * i));
-      const int32_t pg0 = sload_i32(bt + jp0);
+      // ids of the first two pages in one round trip (the second is read only
+      // when the segment has it)
+      sload2_i32(bt + jp0, bt + (jp0 + 1 < jp1 ? jp0 + 1 : jp0), &pg0, &pg_next);
       const char* src_u = uniform(cbase + (int64_t)pg0 * kPageBytesG);
       const uint32_t p_m0 = uniform_lds((LDSP char*)g_page0);
 #pragma unroll
       for (int i = 0; i < 19; ++i)
         if (i < ndma) dma16_u(src_u, offa[i], p_m0 + 1024 * (ln.wave + 4 * i));
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    // Wait for this wave's query loads only (issued before the page's, and
+    // direct loads complete in order): the first page keeps landing while
+    // the queries are read into registers; its own wait is at the page top.
+    if (ndma == 19) asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    barrier_lds();
     // Q^T fragments stay in AGPRs for the whole segment (the MFMAs read them there)
     bf16x8 qf[36];
     {
@@ -358,19 +370,9 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) asm volatile("" : "=a"(qf[kb]) : "0"(t[kb]));
     }
-    __syncthreads();                                             // buffer 1 free again
+    barrier_lds();                                               // buffer 1 free again (page 0 may still land)
 
-    Acc acc;
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc.o[cb][h2][r] = 0.f;
-    acc.m_ref = -INFINITY;
-    acc.l_own = 0.f;
 
-    int32_t pg_next = jp0 + 1 < jp1 ? bt[jp0 + 1] : bt[jp0];      // page ids are read one page ahead
     for (int64_t jp = jp0; jp < jp1; ++jp) {
       const bool even = ((jp - jp0) & 1) == 0;
       LDSP char* buf = even ? (LDSP char*)g_page0 : (LDSP char*)g_page1;

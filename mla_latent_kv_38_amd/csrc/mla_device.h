@@ -149,6 +149,16 @@ __device__ __forceinline__ int32_t sload_i32(const int32_t* p) {
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(u) : "memory");
   return v;
 }
+// Two such loads in flight together (one memory round trip for both).
+__device__ __forceinline__ void sload2_i32(const int32_t* p, const int32_t* q, int32_t* a, int32_t* b) {
+  int32_t va, vb;
+  const char* up = uniform(reinterpret_cast<const char*>(p));
+  const char* uq = uniform(reinterpret_cast<const char*>(q));
+  asm volatile("s_load_dword %0, %2, 0x0\n\ts_load_dword %1, %3, 0x0\n\ts_waitcnt lgkmcnt(0)"
+               : "=&s"(va), "=&s"(vb) : "s"(up), "s"(uq) : "memory");
+  *a = va;
+  *b = vb;
+}
 
 // ---- split-KV schedule -----------------------------------------------------
 // The batch's pages are flattened in sequence order (sequence b owns
@@ -195,6 +205,82 @@ __device__ __forceinline__ void page_prefix(const int32_t* seq_lens, int32_t B, 
   if (t == 0) scan[0] = 0;
   __syncthreads();
   *chunk_out = chunk;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts of
+// 1, 2, 4 and 8 lanes inside each 16-lane row, then the last lane of row 0
+// (row 2) added to row 1 (row 3) and the last lane of row 1 to rows 2 and 3.
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31 -> rows 2, 3
+  return v;
+}
+
+// The part of the split-KV schedule one workgroup needs, in two barriers and
+// no search: the total page count P, the part's page range [x0, x1) and, when
+// the part is not empty, the sequence b owning page x0 and that sequence's
+// first flattened page.  Thread t sums the pages of sequences
+// [t*chunk, (t+1)*chunk); the thread whose range holds x0 publishes it.  With
+// one sequence per thread (chunk == 1) and lens_lds non-null, lens_lds[b] =
+// seq_lens[b] for every b < B afterwards.  Must be called by the whole block.
+struct PartRange {
+  int64_t P, x0, x1, first;
+  int32_t b, chunk;
+};
+__device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, int32_t B, int32_t bs, int64_t part,
+                                                 int64_t W, int32_t* lens_lds) {
+  __shared__ int32_t wave_tot[16];
+  __shared__ int64_t owner[2];
+  const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  PartRange r;
+  r.chunk = (B + nt - 1) / nt;
+  int32_t s = 0;
+  if (r.chunk == 1) {
+    const int32_t L = t < B ? seq_lens[t] : 0;
+    if (lens_lds && t < B) lens_lds[t] = L;
+    s = pages_of(L, bs);
+  } else {
+    for (int32_t b = t * r.chunk; b < min(B, (t + 1) * r.chunk); ++b) s += pages_of(seq_lens[b], bs);
+  }
+  const int32_t v = wave_incl_scan(s);
+  if (lane == 63) wave_tot[wv] = v;
+  __syncthreads();
+  int64_t carry = 0, total = 0;
+  for (int w = 0; w < nt / 64; ++w) {
+    const int32_t c = wave_tot[w];
+    carry += w < wv ? c : 0;
+    total += c;
+  }
+  r.P = total;
+  r.x0 = part_start(part, r.P, W);
+  r.x1 = part_start(part + 1, r.P, W);
+  const int64_t incl = carry + v, excl = incl - s;
+  if (s > 0 && excl <= r.x0 && r.x0 < incl) {        // one thread when x0 < P
+    owner[0] = t;
+    owner[1] = excl;
+  }
+  __syncthreads();
+  r.b = 0;
+  r.first = 0;
+  if (r.x0 < r.x1) {
+    int32_t b = static_cast<int32_t>(owner[0]) * r.chunk;
+    int64_t first = owner[1];
+    if (r.chunk > 1) {
+      for (;;) {
+        const int32_t np = pages_of(seq_lens[b], bs);
+        if (r.x0 < first + np) break;
+        first += np;
+        ++b;
+      }
+    }
+    r.b = b;
+    r.first = first;
+  }
+  return r;
 }
 
 // Sequence owning flattened page x (0 <= x < P), and that sequence's first page.
