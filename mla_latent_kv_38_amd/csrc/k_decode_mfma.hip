@@ -523,58 +523,22 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
   }
 }
 
+// One workgroup per (sequence, head group, wave-column block); the page
+// prefix gives the sequence's part range.  (Placing each workgroup on the XCD
+// whose L2 the partials were written through measured no faster than this
+// plain order once the search it needed was counted.)
 __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32_t W, int32_t HG,
                                                    const int32_t* __restrict__ seq_lens,
                                                    const float* __restrict__ ws_o,
                                                    const float* __restrict__ ws_lse,
                                                    uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
-  __shared__ int32_t scan[257];
-  __shared__ int32_t w0s[256], w1s[256];           // part range of each sequence (one division per thread)
-  int32_t chunk;
-  page_prefix(seq_lens, B, kBs, scan, &chunk);
-  const int64_t P = scan[blockDim.x];
   const int per_seq = HG * 16;
-  if (chunk == 1) {
-    {
-      const int t = threadIdx.x;
-      if (t < B && P > 0) {
-        const int64_t pre = scan[t], np = scan[t + 1] - pre;
-        w0s[t] = (int32_t)min<int64_t>(part_of_page(pre, P, W), W - 1);
-        w1s[t] = np > 0 ? (int32_t)part_of_page(pre + np - 1, P, W) : w0s[t];
-      } else if (t < B) {
-        w0s[t] = w1s[t] = 0;
-      }
-      __syncthreads();
-    }
-    // Items of the sequences whose first part ran on this workgroup's XCD
-    // (the decode kernel gives XCD x the parts [x ppx, (x+1) ppx)), so the
-    // partials are mostly read back from the L2 they were written through.
-    const int ppx = (W + 7) / 8;
-    const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3, J = gridDim.x >> 3;
-    auto key = [&](int32_t bb) -> int { return w0s[bb] / ppx; };
-    auto lower = [&](int x) {                      // first sequence with key >= x
-      int lo = 0, hi = B;
-      while (lo < hi) { const int mid = (lo + hi) >> 1; if (key(mid) < x) lo = mid + 1; else hi = mid; }
-      return lo;
-    };
-    const int b_lo = lower(xcd), b_hi = lower(xcd + 1);
-    const int items = (b_hi - b_lo) * per_seq;
-    for (int it = j; it < items; it += J) {
-      const int32_t b = b_lo + it / per_seq;
-      const int r = it % per_seq;
-      combine_item(b, r / 16, r % 16, n_h, W, P, scan[b + 1] - scan[b], w0s[b], w1s[b], ws_o, ws_lse, o_lat, lse);
-    }
-  } else {
-    for (int it = blockIdx.x; it < B * per_seq; it += gridDim.x) {
-      const int32_t b = it / per_seq;
-      const int r = it % per_seq;
-      int64_t pre = 0;
-      for (int32_t i = 0; i < b; ++i) pre += pages_of(seq_lens[i], kBs);
-      const int64_t np = pages_of(seq_lens[b], kBs);
-      const int64_t w0 = np > 0 ? part_of_page(pre, P, W) : 0, w1 = np > 0 ? part_of_page(pre + np - 1, P, W) : 0;
-      combine_item(b, r / 16, r % 16, n_h, W, P, np, w0, w1, ws_o, ws_lse, o_lat, lse);
-    }
-  }
+  const int32_t b = blockIdx.x / per_seq;
+  const int r = blockIdx.x % per_seq;
+  const SeqPages sp = seq_pages(seq_lens, B, kBs, b);
+  const int64_t w0 = sp.np > 0 ? part_of_page(sp.first, sp.P, W) : 0;
+  const int64_t w1 = sp.np > 0 ? part_of_page(sp.first + sp.np - 1, sp.P, W) : 0;
+  combine_item(b, r / 16, r % 16, n_h, W, sp.P, sp.np, w0, w1, ws_o, ws_lse, o_lat, lse);
 }
 
 }  // namespace
@@ -599,7 +563,7 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
                                        seq_lens, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_h64<<<((B * HG * 16 + 7) / 8) * 8, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, ws_o, ws_lse,
+  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, ws_o, ws_lse,
                                           static_cast<uint16_t*>(o_lat), lse);
   return hipGetLastError();
 }

@@ -283,6 +283,45 @@ __device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, int32_
   return r;
 }
 
+// Total page count P, and the first flattened page and page count of one
+// sequence b, in two barriers.  Must be called by the whole block.
+struct SeqPages {
+  int64_t P, first, np;
+};
+__device__ __forceinline__ SeqPages seq_pages(const int32_t* seq_lens, int32_t B, int32_t bs, int32_t b) {
+  __shared__ int32_t wave_tot[16];
+  __shared__ int64_t found[2];
+  const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int32_t chunk = (B + nt - 1) / nt;
+  const int32_t b0 = t * chunk, b1 = min(B, b0 + chunk);
+  int32_t s = 0, before = 0, mine = 0;                 // pages of the chunk, of its part before b, of b
+  for (int32_t i = b0; i < b1; ++i) {
+    const int32_t np = pages_of(seq_lens[i], bs);
+    before += i < b ? np : 0;
+    mine += i == b ? np : 0;
+    s += np;
+  }
+  const int32_t v = wave_incl_scan(s);
+  if (lane == 63) wave_tot[wv] = v;
+  __syncthreads();
+  int64_t carry = 0, total = 0;
+  for (int w = 0; w < nt / 64; ++w) {
+    const int32_t c = wave_tot[w];
+    carry += w < wv ? c : 0;
+    total += c;
+  }
+  if (b0 <= b && b < b1) {                             // the thread whose chunk holds b
+    found[0] = carry + v - s + before;
+    found[1] = mine;
+  }
+  __syncthreads();
+  SeqPages r;
+  r.P = total;
+  r.first = found[0];
+  r.np = found[1];
+  return r;
+}
+
 // Sequence owning flattened page x (0 <= x < P), and that sequence's first page.
 __device__ __forceinline__ void locate_page(const int32_t* seq_lens, int32_t B, int32_t bs,
                                             const int32_t* scan, int32_t chunk, int64_t x,
