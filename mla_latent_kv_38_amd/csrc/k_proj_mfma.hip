@@ -11,6 +11,7 @@
 //
 // 16x16x32 operand layouts (lane l, group g = l / 16, s = l % 16):
 //   A: A[s][8g + e], e = 0..7      B: B[8g + e][s]      D: D[4g + r][s], r = 0..3
+#include <algorithm>
 #include <cmath>
 
 #include "mla_device.h"
@@ -26,9 +27,6 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #define LDSP __attribute__((address_space(3)))
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
 
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -45,8 +43,13 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const 
 constexpr int kAbsCols = 128;
 constexpr int kAbsRowB = kAbsCols * 2 + 16;     // padded LDS row (bytes)
 
+// The batch may be split over workgroups too (grid z): workgroup z takes
+// rows [z bpw, (z+1) bpw), at most kMaxBlk blocks of 16, all of whose q_C
+// fragments are loaded together with the weight tile.
+constexpr int kMaxBlk = 4;
+
 template <int kKs>   // d_h / 32
-__global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int32_t d_c, int32_t d_R,
+__global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t bpw, int32_t n_h, int32_t d_c, int32_t d_R,
                                                      const uint16_t* __restrict__ q_c,
                                                      const uint16_t* __restrict__ q_r,
                                                      const int32_t* __restrict__ pos,
@@ -57,46 +60,56 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
   const int cblocks = d_c / kAbsCols;
   const int h = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
   const int c0 = cb * kAbsCols;
+  const int b_lo = blockIdx.y * bpw, b_hi = min(B, b_lo + bpw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, s = lane & 15;
   const int64_t D = d_c + d_R;
 
-  // RoPE half of q_abs, pairs spread over the head's workgroups.  The first
-  // pair's inputs are loaded before the weight tile, so its float64 rotation
-  // runs while the tile is in flight (loads complete in order).
+  // RoPE half of q_abs for this workgroup's batch rows, pairs spread over the
+  // head's column-block workgroups (pair i on thread i mod (256 cblocks)).
+  // The inputs of a thread's first kRopePer pairs are loaded before the
+  // weight tile, so their float64 rotations run while the tile is in flight.
+  constexpr int kRopePer = 4;
   const int half = d_R / 2;
+  const int npairs = (b_hi - b_lo) * half;
   const int stride = cblocks * 256;
   const int i_first = cb * 256 + tid;
-  const bool has_pair = i_first < B * half;
-  float r0 = 0.f, r1 = 0.f;
-  int32_t rpos = 0;
-  if (has_pair) {
-    const int bb = i_first / half, p = i_first - bb * half;
-    const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
-    r0 = bf16_to_f32(q_r[src]);
-    r1 = bf16_to_f32(q_r[src + 1]);
-    rpos = pos[bb];
+  float rx[kRopePer][2];
+  int32_t rpos[kRopePer];
+#pragma unroll
+  for (int k = 0; k < kRopePer; ++k) {
+    const int i = i_first + k * stride;
+    rx[k][0] = rx[k][1] = 0.f;
+    rpos[k] = 0;
+    if (i < npairs) {
+      const int bb = b_lo + i / half, p = i % half;
+      const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
+      rx[k][0] = bf16_to_f32(q_r[src]);
+      rx[k][1] = bf16_to_f32(q_r[src + 1]);
+      rpos[k] = pos[bb];
+    }
   }
   auto rope_store = [&](int i, float x0, float x1, int32_t ps) {
-    const int bb = i / half, p = i - bb * half;
+    const int bb = b_lo + i / half, p = i % half;
     float y0, y1;
     rope_pair(x0, x1, ps, p, d_R, log2_base, &y0, &y1);
-    *reinterpret_cast<uint32_t*>(q_abs + ((int64_t)bb * n_h + h) * D + d_c + 2 * p) = pack_bf16(y0, y1);
+    *reinterpret_cast<uint32_t*>(q_abs + ((int64_t)bb * n_h + h) * D + d_c + 2 * p) = pack2_bf16(y0, y1);
   };
 
-  // q_C rows of the first batch block, in flight together with the weight tile
-  auto load_q = [&](int b0, bf16x8 (&qf)[kKs]) {
-    const int b = b0 + s;
+  // q_C rows of the workgroup's batch blocks, in flight together with the weight tile
+  const int nblk = (b_hi - b_lo + 15) / 16;
+  bf16x8 qf[kMaxBlk][kKs];
+#pragma unroll
+  for (int k = 0; k < kMaxBlk; ++k) {
+    const int b = b_lo + 16 * k + s;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      if (b < B)
-        qf[ks] = *reinterpret_cast<const bf16x8*>(q_c + ((int64_t)b * n_h + h) * d_h + 32 * ks + 8 * g);
+      if (k < nblk && b < b_hi)
+        qf[k][ks] = *reinterpret_cast<const bf16x8*>(q_c + ((int64_t)b * n_h + h) * d_h + 32 * ks + 8 * g);
       else
-        qf[ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+        qf[k][ks] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
     }
-  };
-  bf16x8 qf[kKs];
-  load_q(0, qf);
+  }
 
   // stage W_UK[h][:, c0:c0+128] (d_h rows of 256 B): all loads first, then the LDS writes
   {
@@ -107,15 +120,17 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
       const int c = tid + 256 * j, row = c >> 4, ch = c & 15;
       v[j] = *reinterpret_cast<const u32x4*>(w_uk + ((int64_t)h * d_h + row) * d_c + c0 + 8 * ch);
     }
-    if (has_pair) rope_store(i_first, r0, r1, rpos);
+#pragma unroll
+    for (int k = 0; k < kRopePer; ++k)
+      if (i_first + k * stride < npairs) rope_store(i_first + k * stride, rx[k][0], rx[k][1], rpos[k]);
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
       const int c = tid + 256 * j, row = c >> 4, ch = c & 15;
       *reinterpret_cast<LDSP u32x4*>((LDSP char*)tile + row * kAbsRowB + ch * 16) = v[j];
     }
   }
-  for (int i = i_first + stride; i < B * half; i += stride) {   // batches beyond 256 * cblocks pairs
-    const int bb = i / half, p = i - bb * half;
+  for (int i = i_first + kRopePer * stride; i < npairs; i += stride) {
+    const int bb = b_lo + i / half, p = i % half;
     const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
     rope_store(i, bf16_to_f32(q_r[src]), bf16_to_f32(q_r[src + 1]), pos[bb]);
   }
@@ -137,22 +152,22 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
       af[mb][ks] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 
-  for (int b0 = 0; b0 < B; b0 += 16) {
-    const int b = b0 + s;
-    if (b0 > 0) load_q(b0, qf);
+#pragma unroll
+  for (int k = 0; k < kMaxBlk; ++k) {
+    if (k >= nblk) break;
+    const int b = b_lo + 16 * k + s;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < kKs; ++ks) acc = mfma16(af[mb][ks], qf[ks], acc);
-      if (b < B) {
+      for (int ks = 0; ks < kKs; ++ks) acc = mfma16(af[mb][ks], qf[k][ks], acc);
+      if (b < b_hi) {
         const int c = c0 + 32 * wave + 16 * mb + 4 * g;
         *reinterpret_cast<u32x2*>(q_abs + ((int64_t)b * n_h + h) * D + c) =
-            u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+            u32x2{pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3])};
       }
     }
   }
-
 }
 
 // ---------------------------------------------------------------------------
@@ -163,54 +178,64 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t n_h, int
 // and read by all four waves.
 // ---------------------------------------------------------------------------
 template <int kKs>   // d_c / 32
-__global__ void __launch_bounds__(256) up_v_mfma(int32_t B, int32_t n_h, int32_t d_h,
+__global__ void __launch_bounds__(256) up_v_mfma(int32_t B, int32_t bpw, int32_t n_h, int32_t d_h,
                                                  const uint16_t* __restrict__ o_lat,
                                                  const uint16_t* __restrict__ w_uv,
                                                  uint16_t* __restrict__ out) {
   constexpr int d_c = 32 * kKs;
   constexpr int kRowB = d_c * 2 + 16;
-  __shared__ __attribute__((aligned(16))) char otile[16 * kRowB];
+  __shared__ __attribute__((aligned(16))) char otile[2][16 * kRowB];   // double-buffered batch blocks
   const int iblocks = d_h / 64;
   const int h = blockIdx.x / iblocks, ib = blockIdx.x % iblocks;
+  const int b_lo = blockIdx.y * bpw, b_hi = min(B, b_lo + bpw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, s = lane & 15;
   const int i0 = 64 * ib + 16 * wave;
 
+  constexpr int kChunks = 16 * d_c / 8;           // 16-byte chunks of one o_lat tile
+  constexpr int kPer = (kChunks + 255) / 256;
+  auto load_tile = [&](int b0, u32x4 (&v)[kPer]) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = tid + 256 * j, row = c / (d_c / 8), ch = c % (d_c / 8);
+      v[j] = u32x4{0u, 0u, 0u, 0u};
+      if (c < kChunks && b0 + row < b_hi)
+        v[j] = *reinterpret_cast<const u32x4*>(o_lat + ((int64_t)(b0 + row) * n_h + h) * d_c + 8 * ch);
+    }
+  };
+  auto store_tile = [&](int buf, const u32x4 (&v)[kPer]) {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int c = tid + 256 * j, row = c / (d_c / 8), ch = c % (d_c / 8);
+      if (c < kChunks) *reinterpret_cast<LDSP u32x4*>((LDSP char*)otile[buf] + row * kRowB + ch * 16) = v[j];
+    }
+  };
+
+  u32x4 v[kPer];
+  load_tile(b_lo, v);                             // first o_lat block in flight with the weights
   bf16x8 af[kKs];
   {
     const uint16_t* wrow = w_uv + ((int64_t)h * d_h + i0 + s) * d_c + 8 * g;
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) af[ks] = *reinterpret_cast<const bf16x8*>(wrow + 32 * ks);
   }
-
-  constexpr int kChunks = 16 * d_c / 8;           // 16-byte chunks of one o_lat tile
-  for (int b0 = 0; b0 < B; b0 += 16) {
-    if (b0 > 0) __syncthreads();                  // previous tile fully read
-    constexpr int kPer = (kChunks + 255) / 256;
-    u32x4 v[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {             // all loads in flight before the first LDS write
-      const int c = tid + 256 * j, row = c / (d_c / 8), ch = c % (d_c / 8);
-      v[j] = u32x4{0u, 0u, 0u, 0u};
-      if (c < kChunks && b0 + row < B)
-        v[j] = *reinterpret_cast<const u32x4*>(o_lat + ((int64_t)(b0 + row) * n_h + h) * d_c + 8 * ch);
-    }
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) {
-      const int c = tid + 256 * j, row = c / (d_c / 8), ch = c % (d_c / 8);
-      if (c < kChunks) *reinterpret_cast<LDSP u32x4*>((LDSP char*)otile + row * kRowB + ch * 16) = v[j];
-    }
-    __syncthreads();
+  store_tile(0, v);
+  int buf = 0;
+  for (int b0 = b_lo; b0 < b_hi; b0 += 16, buf ^= 1) {
+    const bool more = b0 + 16 < b_hi;
+    if (more) load_tile(b0 + 16, v);              // next block in flight during this one
+    __syncthreads();                              // block b0 staged; the other buffer free
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKs; ++ks) {
-      const bf16x8 xf = *reinterpret_cast<const LDSP bf16x8*>((LDSP char*)otile + s * kRowB + (32 * ks + 8 * g) * 2);
+      const bf16x8 xf = *reinterpret_cast<const LDSP bf16x8*>((LDSP char*)otile[buf] + s * kRowB + (32 * ks + 8 * g) * 2);
       acc = mfma16(af[ks], xf, acc);
     }
     const int b = b0 + s;
-    if (b < B)
+    if (b < b_hi)
       *reinterpret_cast<u32x2*>(out + ((int64_t)b * n_h + h) * d_h + i0 + 4 * g) =
-          u32x2{pack_bf16(acc[0], acc[1]), pack_bf16(acc[2], acc[3])};
+          u32x2{pack2_bf16(acc[0], acc[1]), pack2_bf16(acc[2], acc[3])};
+    if (more) store_tile(buf ^ 1, v);
   }
 }
 
@@ -226,16 +251,23 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, c
   if (d.act_dtype != MLA_BF16 || d.d_latent % kAbsCols != 0 || d.d_head % 32 != 0 || D % 4 != 0 ||
       !aligned16(q_c) || !aligned16(w_uk) || !aligned16(q_abs) || (reinterpret_cast<uintptr_t>(q_r) & 3u))
     return hipSuccess;
-  const dim3 grid(d.n_heads * (d.d_latent / kAbsCols));
+  // Split the batch over workgroups until the grid fills the chip (at most
+  // kMaxBlk blocks of 16 rows per workgroup).
+  const int wgs = d.n_heads * (d.d_latent / kAbsCols);
+  const int nblocks = (B + 15) / 16;
+  int nsplit = std::max((nblocks + kMaxBlk - 1) / kMaxBlk, std::min(nblocks, (256 + wgs - 1) / wgs));
+  const int bpw = 16 * ((nblocks + nsplit - 1) / nsplit);
+  nsplit = (B + bpw - 1) / bpw;
+  const dim3 grid(wgs, nsplit);
   auto qc = static_cast<const uint16_t*>(q_c);
   auto qr = static_cast<const uint16_t*>(q_r);
   auto w = static_cast<const uint16_t*>(w_uk);
   auto qa = static_cast<uint16_t*>(q_abs);
   switch (d.d_head) {
-    case 64:  absorb_q_mfma<2><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
-    case 128: absorb_q_mfma<4><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
-    case 192: absorb_q_mfma<6><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
-    case 256: absorb_q_mfma<8><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 64:  absorb_q_mfma<2><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 128: absorb_q_mfma<4><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 192: absorb_q_mfma<6><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 256: absorb_q_mfma<8><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
     default: return hipSuccess;
   }
   *handled = true;
@@ -248,14 +280,19 @@ hipError_t launch_up_v_mfma(const mla_dims& d, int32_t B, const void* o_lat, con
   if (d.act_dtype != MLA_BF16 || d.d_head % 64 != 0 || !aligned16(o_lat) || !aligned16(w_uv) ||
       (reinterpret_cast<uintptr_t>(out) & 7u))
     return hipSuccess;
-  const dim3 grid(d.n_heads * (d.d_head / 64));
+  // Split the batch over workgroups until the grid fills the chip.
+  const int wgs = d.n_heads * (d.d_head / 64);
+  const int nblocks = (B + 15) / 16;
+  const int nsplit0 = std::min(nblocks, (256 + wgs - 1) / wgs);
+  const int bpw = 16 * ((nblocks + nsplit0 - 1) / nsplit0);
+  const dim3 grid(wgs, (B + bpw - 1) / bpw);
   auto o = static_cast<const uint16_t*>(o_lat);
   auto w = static_cast<const uint16_t*>(w_uv);
   auto y = static_cast<uint16_t*>(out);
   switch (d.d_latent) {
-    case 128: up_v_mfma<4><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_head, o, w, y); break;
-    case 256: up_v_mfma<8><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_head, o, w, y); break;
-    case 512: up_v_mfma<16><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_head, o, w, y); break;
+    case 128: up_v_mfma<4><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_head, o, w, y); break;
+    case 256: up_v_mfma<8><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_head, o, w, y); break;
+    case 512: up_v_mfma<16><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_head, o, w, y); break;
     default: return hipSuccess;
   }
   *handled = true;

@@ -54,7 +54,7 @@ def _f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-CASES = [(128, 1), (128, 16), (128, 17), (128, 40), (16, 128), (16, 33)]
+CASES = [(128, 1), (128, 16), (128, 17), (128, 40), (128, 100), (16, 128), (16, 33), (16, 300)]
 
 
 @pytest.mark.parametrize("n_h,B", CASES)
