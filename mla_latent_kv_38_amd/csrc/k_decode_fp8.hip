@@ -52,12 +52,13 @@ __shared__ int32_t g_lens[256];
 __shared__ float g_xm[4][kHeads];           // per-wave reference max (segment merge)
 __shared__ float g_xl[4][kHeads];           // per-wave row sums
 
-__device__ __forceinline__ uint32_t pack_bf16_rne(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
-// Two float32 holding bfloat16 values exactly: keep the upper halves.
-__device__ __forceinline__ uint32_t pack_exact(f32x2 v) {
-  return (__float_as_uint(v[0]) >> 16) | (__float_as_uint(v[1]) & 0xFFFF0000u);
+// Two E4M3 codes (the low or high half of a dword) -> two bfloat16 in one
+// instruction: the scaled conversion with scale 1.0, exact for every code
+// (each E4M3 value is a bfloat16 value; checked on the device against the
+// float32 conversion for all 65 536 code pairs).
+template <bool kHi>
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, kHi));
 }
 
 // One page: codes (36 x 64 lanes x 16 B; wave w issues k = w, w+4, ...) and,
@@ -89,14 +90,8 @@ __device__ __forceinline__ void convert_page(const LDSP char* __restrict__ f8, L
   for (int i = i0; i < i0 + 3; ++i) {
     const int c = tid + 256 * i, row = c / 36, ch = c - 36 * row;
     const uint32_t keep = row < nvalid ? 0xFFFFFFFFu : 0u;     // branch-free zeroing of rows past the end
-    u32x4 lo = {pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][0], false)),
-                pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][0], true)),
-                pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][1], false)),
-                pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][1], true))};
-    u32x4 hi = {pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][2], false)),
-                pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][2], true)),
-                pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][3], false)),
-                pack_exact(__builtin_amdgcn_cvt_pk_f32_fp8(v[i][3], true))};
+    u32x4 lo = {cvt_pair<false>(v[i][0]), cvt_pair<true>(v[i][0]), cvt_pair<false>(v[i][1]), cvt_pair<true>(v[i][1])};
+    u32x4 hi = {cvt_pair<false>(v[i][2]), cvt_pair<true>(v[i][2]), cvt_pair<false>(v[i][3]), cvt_pair<true>(v[i][3])};
     lo &= keep;
     hi &= keep;
     LDSP char* dst = tile + row * kRowB + ch * 32;
@@ -107,7 +102,7 @@ __device__ __forceinline__ void convert_page(const LDSP char* __restrict__ f8, L
 }
 
 struct State {                     // one wave's running state for its token block
-  f32x4 o[32];                     // O^T blocks: columns 16 cb + 4 g + r, head s
+  f32x4 o[32];                     // O^T blocks: columns 16 cb + 4 g + r, head s (AGPRs)
   float m_ref, l_part;             // reference max (log2 units) of head s; partial row sum
 };
 
@@ -139,8 +134,7 @@ __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ tile,
     v[r] = t < nvalid ? S[r] * s2 * scl[r] : -INFINITY;
     mb = fmaxf(mb, v[r]);
   }
-  mb = fmaxf(mb, __shfl_xor(mb, 16));
-  mb = fmaxf(mb, __shfl_xor(mb, 32));
+  mb = max_xor32(max_xor16(mb));
   float alpha = 1.f;
   if (mb > st.m_ref + kTau) {
     alpha = __builtin_amdgcn_exp2f(st.m_ref - mb);
@@ -160,15 +154,22 @@ __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ tile,
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) st.o[cb] *= alpha;
   }
-  const u32x2 pk = {pack_bf16_rne(p[0], p[1]), pack_bf16_rne(p[2], p[3])};
+  const u32x2 pk = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3])};
   const s16x4 pf = __builtin_bit_cast(s16x4, pk);
   // V^T[16 cols x 16 tok]: in each 16-lane group, source lane s' names row
   // 16w + 4g + s'/4 and columns 16 cb + 4 (s'%4) .. +3; lane s receives column s.
   const LDSP char* vp = tile + (16 * wave + 4 * g + (s >> 2)) * kRowB + 4 * (s & 3) * 2;
+  // V^T fragments kVPre blocks ahead; the accumulators live in AGPRs (the
+  // MFMA reads and writes them there), which leaves the VGPRs for the reads.
+  constexpr int kVPre = 8;
+  s16x4 vf[kVPre];
+#pragma unroll
+  for (int k = 0; k < kVPre; ++k) vf[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + 32 * k));
+  asm volatile("s_nop 4" ::: "memory");                          // P (VALU) -> MFMA source
 #pragma unroll
   for (int cb = 0; cb < 32; ++cb) {
-    const s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + 32 * cb));
-    asm volatile("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+v"(st.o[cb]) : "v"(a), "v"(pf));
+    asm volatile("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(st.o[cb]) : "v"(vf[cb % kVPre]), "v"(pf));
+    if (cb + kVPre < 32) vf[cb % kVPre] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + 32 * (cb + kVPre)));
   }
 }
 
@@ -300,7 +301,7 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
       const int col = 16 * cb + 4 * g;
       if (whole)
         *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
-            u32x2{pack_bf16_rne(o[0], o[1]), pack_bf16_rne(o[2], o[3])};
+            u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
       else
         *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + head) * kDc + col) = o;
     }
