@@ -4,22 +4,24 @@
 //
 // Dequantisation factors out of both contractions: with row = s_t * c~_t,
 //   score_t = s_t * (q . c~_t)   and   o = sum_t (p_t s_t) c~_t / sum_t p_t,
-// so the kernel converts the E4M3 codes to bfloat16 exactly (every E4M3 value
-// is a bfloat16 value) and applies s_t to the score and to P in float32.
+// so the kernel converts E4M3 codes to bfloat16 exactly (every E4M3 value is
+// a bfloat16 value) right before each MFMA and applies s_t to the score and
+// to P in float32.
 //
-// Per page (one workgroup = 4 waves on one CU):
-//   * the 36 KiB of codes and 256 B of scales arrive by direct loads into one
-//     of two staging buffers (the next page is in flight meanwhile);
-//   * a conversion pass writes the bf16 tile (64 rows padded to 73 x 16 B),
-//     zeroing rows past the end of the sequence;
-//   * wave w owns tokens 16w..16w+15 of every page with its own online
-//     softmax state, so no score or maximum crosses waves:
-//       QK  S^T[16 tok x 16 heads] = C . Q^T: 18 v_mfma_f32_16x16x32_bf16,
-//           Q^T in registers;
-//       PV  O^T[512 x 16 heads] += V^T[512 x 16 tok] . P^T: 32
-//           v_mfma_f32_16x16x16_bf16, V^T by ds_read_b64_tr_b16 and P^T taken
-//           straight from the QK result registers (the D layout of the score
-//           MFMA is the B layout of the PV MFMA).
+// Pages stream HBM -> LDS by direct loads through a ring of four slots
+// (codes in rows padded to 37 x 16 B, plus the 64 scales), three pages ahead
+// of the one being computed.  Wave w owns tokens 16w..16w+15 of every page
+// with its own online softmax state, so no score or maximum crosses waves
+// and a page needs one barrier:
+//   QK  S^T[16 tok x 16 heads] = C . Q^T: 18 v_mfma_f32_16x16x32_bf16, the A
+//       fragments read as 8 codes per lane and converted in registers, Q^T in
+//       AGPRs;
+//   PV  O^T[512 x 16 heads] += V^T[512 x 16 tok] . P^T: 32
+//       v_mfma_f32_16x16x16_bf16 with accumulators in AGPRs; V^T comes from
+//       ds_read_b64_tr_b8 (one read gives two 16-column blocks of the wave's
+//       tokens), converted in registers; P^T is taken straight from the QK
+//       result registers (the D layout of the score MFMA is the B layout of
+//       the PV MFMA).
 // At the end of a segment the four waves' states are merged through LDS.
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -29,8 +31,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 #define LDSP __attribute__((address_space(3)))
@@ -39,15 +41,14 @@ constexpr int kD = 576;
 constexpr int kDc = 512;
 constexpr int kBs = 64;
 constexpr int kHeads = 16;                  // heads per workgroup
-constexpr int kRowB = 1168;                 // bf16 tile row: 1152 B + 16 pad
-constexpr int kF8B = kBs * kD;              // 36864 B of codes per page = 36 x 1 KiB
+constexpr int kRowF = 592;                  // LDS code row: 576 B + 16 pad (37 x 16 B)
+constexpr int kSlotB = kBs * kRowF;         // 37888 B = 37 x 1 KiB
+constexpr int kRing = 4;
+constexpr int64_t kPageG = (int64_t)kBs * kD;  // 36864 B of codes per page in memory
 constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
 
-__shared__ __attribute__((aligned(1024))) char g_f8a[kF8B];
-__shared__ __attribute__((aligned(1024))) char g_f8b[kF8B];
-__shared__ __attribute__((aligned(256))) float g_sca[kBs];
-__shared__ __attribute__((aligned(256))) float g_scb[kBs];
-__shared__ __attribute__((aligned(1024))) char g_tile[kBs * kRowB];
+__shared__ __attribute__((aligned(1024))) char g_ring[kRing * kSlotB];
+__shared__ __attribute__((aligned(256))) float g_sc[kRing][kBs];
 __shared__ int32_t g_lens[256];
 __shared__ float g_xm[4][kHeads];           // per-wave reference max (segment merge)
 __shared__ float g_xl[4][kHeads];           // per-wave row sums
@@ -60,44 +61,51 @@ template <bool kHi>
 __device__ __forceinline__ uint32_t cvt_pair(uint32_t codes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, kHi));
 }
-
-// One page: codes (36 x 64 lanes x 16 B; wave w issues k = w, w+4, ...) and,
-// from wave 0, the 64 scales (64 lanes x 4 B).
-__device__ __forceinline__ void dma_page(const char* src, const float* ssrc, LDSP char* dst,
-                                         LDSP float* sdst, int wave, int lane) {
-#pragma unroll
-  for (int i = 0; i < 9; ++i) {
-    const int k = wave + 4 * i;
-    dma16(src, 1024 * k + 16 * lane, dst + 1024 * k);
-  }
-  if (wave == 0) dma4(reinterpret_cast<const char*>(ssrc), 4 * lane, sdst);
+__device__ __forceinline__ bf16x8 cvt8(i32x2 c) {      // 8 codes -> 8 bfloat16
+  return __builtin_bit_cast(bf16x8, u32x4{cvt_pair<false>(c[0]), cvt_pair<true>(c[0]),
+                                          cvt_pair<false>(c[1]), cvt_pair<true>(c[1])});
 }
 
-// Codes -> bfloat16 tile.  Thread t converts 16-byte chunks t + 256 i of the
-// page (row c / 36, chunk c % 36); rows at or past nvalid are written as zeros
-// so that masked tokens contribute exact zeros to PV.
-__device__ __forceinline__ void convert_page(const LDSP char* __restrict__ f8, LDSP char* __restrict__ tile,
-                                             int nvalid, int tid) {
+// Page loads: LDS slot position q = 64 k + lane of a ring slot holds code row
+// q / 37, 16-B chunk q % 37 (chunk 36 is row padding and re-reads offset 0).
+// Wave w issues loads k = w, w + 4, ... (10 for wave 0, 9 otherwise, 37 in
+// all); wave 0 also loads the 64 scales.  The per-lane source offsets are the
+// same for every page, so they are computed once and kept in AGPRs.
+__device__ __forceinline__ int page_loads(int wave) { return wave == 0 ? 11 : 9; }   // vmcnt per page
+
+__device__ __forceinline__ void page_offsets(int wave, int lane, uint32_t (&off)[10]) {
+  const int q0 = 64 * wave + lane;
+  int row = q0 / 37, ch = q0 - 37 * row;
 #pragma unroll
-  for (int i0 = 0; i0 < 9; i0 += 3) {
-  u32x4 v[9];
-#pragma unroll
-  for (int i = i0; i < i0 + 3; ++i) {
-    const int c = tid + 256 * i, row = c / 36, ch = c - 36 * row;
-    v[i] = *reinterpret_cast<const LDSP u32x4*>(f8 + row * kD + ch * 16);
+  for (int i = 0; i < 10; ++i) {
+    const uint32_t o = (row < kBs && ch != 36) ? static_cast<uint32_t>(row * kD + ch * 16) : 0u;
+    asm volatile("" : "=a"(off[i]) : "0"(o));
+    row += 6;                                    // 256 positions = 6 rows + 34 chunks
+    ch += 34;
+    if (ch >= 37) { ch -= 37; row += 1; }
   }
+}
+
+__device__ __forceinline__ void load_page(const char* src_u, const float* ssrc, int slot, const uint32_t (&off)[10],
+                                          int wave, int lane) {
+  const uint32_t m0 = uniform_lds((LDSP char*)g_ring + slot * kSlotB);
 #pragma unroll
-  for (int i = i0; i < i0 + 3; ++i) {
-    const int c = tid + 256 * i, row = c / 36, ch = c - 36 * row;
-    const uint32_t keep = row < nvalid ? 0xFFFFFFFFu : 0u;     // branch-free zeroing of rows past the end
-    u32x4 lo = {cvt_pair<false>(v[i][0]), cvt_pair<true>(v[i][0]), cvt_pair<false>(v[i][1]), cvt_pair<true>(v[i][1])};
-    u32x4 hi = {cvt_pair<false>(v[i][2]), cvt_pair<true>(v[i][2]), cvt_pair<false>(v[i][3]), cvt_pair<true>(v[i][3])};
-    lo &= keep;
-    hi &= keep;
-    LDSP char* dst = tile + row * kRowB + ch * 32;
-    *reinterpret_cast<LDSP u32x4*>(dst) = lo;
-    *reinterpret_cast<LDSP u32x4*>(dst + 16) = hi;
-  }
+  for (int i = 0; i < 10; ++i)
+    if (wave + 4 * i < 37) dma16_u(src_u, off[i], m0 + 1024 * (wave + 4 * i));
+  if (wave == 0) dma4(reinterpret_cast<const char*>(ssrc), 4 * lane, (LDSP float*)g_sc[slot]);
+}
+
+// Wait until at most `pending` of this wave's loads are in flight (a whole
+// number of pages: 9 or 11 loads each).
+__device__ __forceinline__ void wait_loads(int pending) {
+  switch (pending) {
+    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    case 9: asm volatile("s_waitcnt vmcnt(9)" ::: "memory"); break;
+    case 11: asm volatile("s_waitcnt vmcnt(11)" ::: "memory"); break;
+    case 18: asm volatile("s_waitcnt vmcnt(18)" ::: "memory"); break;
+    case 22: asm volatile("s_waitcnt vmcnt(22)" ::: "memory"); break;
+    case 27: asm volatile("s_waitcnt vmcnt(27)" ::: "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(33)" ::: "memory"); break;
   }
 }
 
@@ -106,22 +114,24 @@ struct State {                     // one wave's running state for its token blo
   float m_ref, l_part;             // reference max (log2 units) of head s; partial row sum
 };
 
-// QK, softmax and PV of one page for wave w's 16 tokens (tile already in LDS).
-__device__ __forceinline__ void page_compute(const LDSP char* __restrict__ tile, const LDSP float* __restrict__ sc,
+// QK, softmax and PV of one page for wave w's 16 tokens (codes in `slot`).
+__device__ __forceinline__ void page_compute(const LDSP char* __restrict__ codes, const LDSP float* __restrict__ sc,
                                              const bf16x8 (&qf)[18], int wave, int lane, int nvalid,
                                              float s2, State& st) {
   const int g = lane >> 4, s = lane & 15;
-  // S^T[tok 16w + 4g + r][head s]
+  // S^T[tok 16w + 4g + r][head s]; lane (g, s) reads token row 16w + s, codes 32 ks + 8g..+7
   f32x4 S = {0.f, 0.f, 0.f, 0.f};
   {
-    const LDSP char* ap = tile + (16 * wave + s) * kRowB + g * 16;
-    bf16x8 af[4];
+    const LDSP char* ap = codes + (16 * wave + s) * kRowF + g * 8;
+    constexpr int kPre = 6;
+    i32x2 af[kPre];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) af[k] = *reinterpret_cast<const LDSP bf16x8*>(ap + 64 * k);
+    for (int k = 0; k < kPre; ++k) af[k] = *reinterpret_cast<const LDSP i32x2*>(ap + 32 * k);
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
-      asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(af[ks & 3]), "a"(qf[ks]));
-      if (ks + 4 < 18) af[ks & 3] = *reinterpret_cast<const LDSP bf16x8*>(ap + 64 * (ks + 4));
+      const bf16x8 a = cvt8(af[ks % kPre]);
+      if (ks + kPre < 18) af[ks % kPre] = *reinterpret_cast<const LDSP i32x2*>(ap + 32 * (ks + kPre));
+      asm volatile("s_nop 1\n v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "a"(qf[ks]));
     }
     asm volatile("s_nop 7\n s_nop 7\n s_nop 1" ::: "memory");   // MFMA result -> VALU
   }
@@ -156,47 +166,29 @@ __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ tile,
   }
   const u32x2 pk = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3])};
   const s16x4 pf = __builtin_bit_cast(s16x4, pk);
-  // V^T[16 cols x 16 tok]: in each 16-lane group, source lane s' names row
-  // 16w + 4g + s'/4 and columns 16 cb + 4 (s'%4) .. +3; lane s receives column s.
-  const LDSP char* vp = tile + (16 * wave + 4 * g + (s >> 2)) * kRowB + 4 * (s & 3) * 2;
-  // V^T fragments kVPre blocks ahead; the accumulators live in AGPRs (the
-  // MFMA reads and writes them there), which leaves the VGPRs for the reads.
-  constexpr int kVPre = 8;
-  s16x4 vf[kVPre];
-#pragma unroll
-  for (int k = 0; k < kVPre; ++k) vf[k] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + 32 * k));
-  asm volatile("s_nop 4" ::: "memory");                          // P (VALU) -> MFMA source
-#pragma unroll
-  for (int cb = 0; cb < 32; ++cb) {
-    asm volatile("v_mfma_f32_16x16x16_bf16 %0, %1, %2, %0" : "+a"(st.o[cb]) : "v"(vf[cb % kVPre]), "v"(pf));
-    if (cb + kVPre < 32) vf[cb % kVPre] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + 32 * (cb + kVPre)));
-  }
-}
 
-// One page.  kEven selects the staging buffers statically (page jp in A, the
-// next page's loads into B, or the reverse), so the compiler can see that the
-// in-flight loads never alias what this page reads.
-template <bool kEven>
-__device__ __forceinline__ void page_iter(int64_t jp, int64_t jp1, int32_t L, const int32_t* bt,
-                                          int32_t& pg_next, const char* cbase, const float* kv_scale,
-                                          const bf16x8 (&qf)[18], int wave, int lane, int tid, float s2,
-                                          State& st) {
-  LDSP char* cur = kEven ? (LDSP char*)g_f8a : (LDSP char*)g_f8b;
-  LDSP char* nxt = kEven ? (LDSP char*)g_f8b : (LDSP char*)g_f8a;
-  LDSP float* csc = kEven ? (LDSP float*)g_sca : (LDSP float*)g_scb;
-  LDSP float* nsc = kEven ? (LDSP float*)g_scb : (LDSP float*)g_sca;
-  const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - jp * kBs);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");             // this wave's loads of page jp
-  barrier_lds();                                                // everyone's; tile free again
-  if (jp + 1 < jp1) {                                           // page jp+1 (its id was read one page ago)
-    const int64_t pg = pg_next;
-    dma_page(cbase + pg * kF8B, kv_scale + pg * kBs, nxt, nsc, wave, lane);
+  // V^T: in each 16-lane group g, source lane j names token row 16w + 4g +
+  // (j/2 mod 4) and the 8 columns 32 c + 8 (j mod 2) + 16 (j/8); lane s then
+  // receives, for tokens 16w + 4g + e, e = 0..3, column 32 c + s (first dword)
+  // and column 32 c + 16 + s (second dword).  Rows past the end of the
+  // sequence are zeroed after conversion (their codes may be anything).
+  const int jj = lane & 15;
+  const LDSP char* vp = codes + (16 * wave + 4 * g + ((jj >> 1) & 3)) * kRowF + 8 * (jj & 1) + 16 * (jj >> 3);
+  const uint32_t keep01 = (16 * wave + 4 * g + 1 < nvalid) ? 0xFFFFFFFFu : (16 * wave + 4 * g < nvalid ? 0x0000FFFFu : 0u);
+  const uint32_t keep23 = (16 * wave + 4 * g + 3 < nvalid) ? 0xFFFFFFFFu : (16 * wave + 4 * g + 2 < nvalid ? 0x0000FFFFu : 0u);
+  constexpr int kVPre = 4;
+  i32x2 vf[kVPre];
+#pragma unroll
+  for (int k = 0; k < kVPre; ++k) vf[k] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vp + 32 * k));
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const i32x2 w = vf[c % kVPre];
+    if (c + kVPre < 16) vf[c % kVPre] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vp + 32 * (c + kVPre)));
+    const s16x4 a0 = __builtin_bit_cast(s16x4, u32x2{cvt_pair<false>(w[0]) & keep01, cvt_pair<true>(w[0]) & keep23});
+    const s16x4 a1 = __builtin_bit_cast(s16x4, u32x2{cvt_pair<false>(w[1]) & keep01, cvt_pair<true>(w[1]) & keep23});
+    asm volatile("s_nop 1\n v_mfma_f32_16x16x16_bf16 %0, %2, %4, %0\n v_mfma_f32_16x16x16_bf16 %1, %3, %4, %1"
+                 : "+a"(st.o[2 * c]), "+a"(st.o[2 * c + 1]) : "v"(a0), "v"(a1), "v"(pf));
   }
-  const int32_t pg_after = jp + 2 < jp1 ? bt[jp + 2] : 0;      // in flight during this page
-  convert_page(cur, (LDSP char*)g_tile, nvalid, tid);
-  barrier_lds();                                                // tile ready
-  page_compute((const LDSP char*)g_tile, csc, qf, wave, lane, nvalid, s2, st);
-  pg_next = pg_after;
 }
 
 __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
@@ -223,49 +215,73 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
   const int64_t x1 = pr.x1;
   int64_t x = pr.x0;
   if (x >= x1) return;
-  int32_t b = pr.b;
+  int32_t b = __builtin_amdgcn_readfirstlane(pr.b);
   int64_t first = pr.first;
 
+  uint32_t off[10];
+  page_offsets(wave, lane, off);
   const char* cbase = reinterpret_cast<const char*>(cache);
+  const int nper = page_loads(wave);
   for (;;) {
-    const int32_t L = seq_len(b);
+    const int32_t L = __builtin_amdgcn_readfirstlane(seq_len(b));
     const int64_t np = pages_of(L, kBs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
+    const int n = static_cast<int>(jp1 - jp0);                  // pages of this segment
     const int32_t* bt = block_table + (int64_t)b * max_pages;
 
+    // The segment's first three pages into slots 0-2, and this head group's
+    // 16 query rows (18 KiB, contiguous in q_abs) into slot 3, which is free
+    // until page 3 is issued: queries and pages arrive in one round trip.
+    const int npre = min(3, n);
     {
-      const int64_t pg = bt[jp0];
-      dma_page(cbase + pg * kF8B, kv_scale + pg * kBs, (LDSP char*)g_f8a, (LDSP float*)g_sca, wave, lane);
+      int32_t pid[3];
+      sload3_i32(bt + jp0, bt + jp0 + min(1, n - 1), bt + jp0 + min(2, n - 1), &pid[0], &pid[1], &pid[2]);
+      const char* q_u = uniform(reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * kHeads) * kD));
+      const uint32_t q_m0 = uniform_lds((LDSP char*)g_ring + 3 * kSlotB);
+#pragma unroll
+      for (int i = 0; i < 5; ++i)
+        if (wave + 4 * i < 18) dma16_u(q_u, 1024 * (wave + 4 * i) + 16 * lane, q_m0 + 1024 * (wave + 4 * i));
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+        if (i < npre)
+          load_page(uniform(cbase + (int64_t)pid[i] * kPageG), kv_scale + (int64_t)pid[i] * kBs, i, off, wave, lane);
     }
-    bf16x8 qf[18];                                              // Q^T, pinned in AGPRs
+    wait_loads(nper * npre);                                    // this wave's query loads
+    barrier_lds();
+    bf16x8 qf[18];                                              // Q^T of heads 16 hg + s, pinned in AGPRs
     {
-      const bf16x8* qsrc = reinterpret_cast<const bf16x8*>(
-          q_abs + ((int64_t)b * n_h + (int64_t)hg * kHeads + s) * kD + 8 * g);
+      const LDSP char* qrow = (LDSP char*)g_ring + 3 * kSlotB + s * (kD * 2) + 16 * g;
       bf16x8 t[18];
 #pragma unroll
-      for (int ks = 0; ks < 18; ++ks) t[ks] = qsrc[4 * ks];
+      for (int ks = 0; ks < 18; ++ks) t[ks] = *reinterpret_cast<const LDSP bf16x8*>(qrow + 64 * ks);
 #pragma unroll
       for (int ks = 0; ks < 18; ++ks) asm volatile("" : "=a"(qf[ks]) : "0"(t[ks]));
     }
+    auto issue = [&](int i) {                                   // page i of the segment into slot i % 4
+      const int32_t pg = sload_i32(bt + jp0 + i);
+      load_page(uniform(cbase + (int64_t)pg * kPageG), kv_scale + (int64_t)pg * kBs, i & 3, off, wave, lane);
+    };
+
     State st;
 #pragma unroll
     for (int cb = 0; cb < 32; ++cb) st.o[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m_ref = -INFINITY;
     st.l_part = 0.f;
 
-    int32_t pg_next = jp0 + 1 < jp1 ? bt[jp0 + 1] : 0;
-    for (int64_t jp = jp0; jp < jp1; jp += 2) {
-      page_iter<true>(jp, jp1, L, bt, pg_next, cbase, kv_scale, qf, wave, lane, tid, s2, st);
-      if (jp + 1 < jp1) page_iter<false>(jp + 1, jp1, L, bt, pg_next, cbase, kv_scale, qf, wave, lane, tid, s2, st);
+    for (int i = 0; i < n; ++i) {
+      wait_loads(nper * min(2, n - 1 - i));                     // this wave's loads of page i
+      barrier_lds();                                            // everyone's; slot of page i-1 free
+      if (i + 3 < n) issue(i + 3);
+      const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - (jp0 + i) * kBs);
+      page_compute((const LDSP char*)g_ring + (i & 3) * kSlotB, (const LDSP float*)g_sc[i & 3], qf, wave, lane,
+                   nvalid, s2, st);
     }
 
     // ---- merge the four waves' states, normalise, store ----------------------
     asm volatile("s_nop 7\n s_nop 7\n s_nop 1" ::: "memory");    // MFMA results -> VALU
-    float lw = st.l_part;
-    lw += __shfl_xor(lw, 16);
-    lw += __shfl_xor(lw, 32);
-    __syncthreads();                                            // every wave done with the tile
+    const float lw = sum_xor32(sum_xor16(st.l_part));
+    __syncthreads();                                            // every wave done with the ring
     if (g == 0) { g_xm[wave][s] = st.m_ref; g_xl[wave][s] = lw; }
     __syncthreads();
     float M = -INFINITY;
@@ -278,14 +294,9 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
       Lsum += mw == -INFINITY ? 0.f : g_xl[w][s] * __builtin_amdgcn_exp2f(mw - M);
     }
     const float fw = (st.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - M)) / Lsum;
-    // wave w's scaled O^T into region w (register order: [cb][lane] float4)
-    auto region = [](int w) -> LDSP f32x4* {
-      LDSP char* r = w == 0 ? (LDSP char*)g_tile : w == 1 ? (LDSP char*)g_tile + 32768
-                   : w == 2 ? (LDSP char*)g_f8a : (LDSP char*)g_f8b;
-      return reinterpret_cast<LDSP f32x4*>(r);
-    };
+    // wave w's scaled O^T into ring slot w (register order: [cb][lane] float4, 32 KiB)
     {
-      LDSP f32x4* dst = region(wave);
+      LDSP f32x4* dst = reinterpret_cast<LDSP f32x4*>((LDSP char*)g_ring + wave * kSlotB);
 #pragma unroll
       for (int cb = 0; cb < 32; ++cb) dst[cb * 64 + lane] = st.o[cb] * fw;
     }
@@ -297,7 +308,7 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
       const int cb = 8 * wave + k;
       f32x4 o = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int w = 0; w < 4; ++w) o += region(w)[cb * 64 + lane];
+      for (int w = 0; w < 4; ++w) o += reinterpret_cast<const LDSP f32x4*>((LDSP char*)g_ring + w * kSlotB)[cb * 64 + lane];
       const int col = 16 * cb + 4 * g;
       if (whole)
         *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
@@ -313,9 +324,9 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
 
     x += jp1 - jp0;
     if (x >= x1) break;
-    do { ++b; } while (pages_of(seq_len(b), kBs) == 0);
+    do { ++b; } while (pages_of(__builtin_amdgcn_readfirstlane(seq_len(b)), kBs) == 0);
     first = x;
-    __syncthreads();                                            // regions read before the next DMA
+    __syncthreads();                                            // slots read before the next loads
   }
 }
 

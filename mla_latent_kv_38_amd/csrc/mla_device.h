@@ -149,6 +149,20 @@ __device__ __forceinline__ int32_t sload_i32(const int32_t* p) {
   asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(u) : "memory");
   return v;
 }
+// Three such loads in flight together.
+__device__ __forceinline__ void sload3_i32(const int32_t* p, const int32_t* q, const int32_t* r, int32_t* a,
+                                           int32_t* b, int32_t* c) {
+  int32_t va, vb, vc;
+  const char* up = uniform(reinterpret_cast<const char*>(p));
+  const char* uq = uniform(reinterpret_cast<const char*>(q));
+  const char* ur = uniform(reinterpret_cast<const char*>(r));
+  asm volatile("s_load_dword %0, %3, 0x0\n\ts_load_dword %1, %4, 0x0\n\ts_load_dword %2, %5, 0x0\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&s"(va), "=&s"(vb), "=&s"(vc) : "s"(up), "s"(uq), "s"(ur) : "memory");
+  *a = va;
+  *b = vb;
+  *c = vc;
+}
 // Two such loads in flight together (one memory round trip for both).
 __device__ __forceinline__ void sload2_i32(const int32_t* p, const int32_t* q, int32_t* a, int32_t* b) {
   int32_t va, vb;
