@@ -117,6 +117,63 @@ __global__ void __launch_bounds__(64) cache_append_generic(int32_t d_c, int32_t 
   }
 }
 
+// The DeepSeek-V2 row (d_c = 512, d_R = 64) from bfloat16 inputs: lane l
+// holds latent elements 8l..8l+7 (one 16-B load) and, for l < 32, RoPE pair
+// l, so the row takes one load and one store instruction per part.  A bf16
+// cache receives the latent bits unchanged (bf16 -> float -> bf16 is exact).
+template <int KV>
+__global__ void __launch_bounds__(64) cache_append_576(const uint16_t* __restrict__ c_kv,
+                                                       const uint16_t* __restrict__ k_r,
+                                                       const int32_t* __restrict__ pos,
+                                                       const int64_t* __restrict__ slot,
+                                                       void* __restrict__ cache,
+                                                       float* __restrict__ kv_scale, double log2_base) {
+  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+  constexpr int kDc = 512, kDr = 64, kD = 576;
+  const int t = blockIdx.x, lane = threadIdx.x;
+  const u32x4_t c = *reinterpret_cast<const u32x4_t*>(c_kv + (int64_t)t * kDc + 8 * lane);
+  uint32_t kp = 0;
+  if (lane < kDr / 2) kp = *reinterpret_cast<const uint32_t*>(k_r + (int64_t)t * kDr + 2 * lane);
+  const int32_t p = pos[t];
+  const int64_t sl = slot[t];
+  float y0 = 0.f, y1 = 0.f;
+  if (lane < kDr / 2)
+    rope_pair(bf16_to_f32(static_cast<uint16_t>(kp & 0xFFFFu)), bf16_to_f32(static_cast<uint16_t>(kp >> 16)), p, lane,
+              kDr, log2_base, &y0, &y1);
+  if constexpr (KV == MLA_BF16) {
+    uint16_t* dst = static_cast<uint16_t*>(cache) + sl * kD;
+    *reinterpret_cast<u32x4_t*>(dst + 8 * lane) = c;
+    if (lane < kDr / 2)
+      *reinterpret_cast<uint32_t*>(dst + kDc + 2 * lane) =
+          static_cast<uint32_t>(f32_to_bf16(y0)) | (static_cast<uint32_t>(f32_to_bf16(y1)) << 16);
+  } else {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(c[i] << 16);
+      x[2 * i + 1] = __uint_as_float(c[i] & 0xFFFF0000u);
+    }
+    float amax = fmaxf(fabsf(y0), fabsf(y1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = wave_max_all(amax);
+    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    uint8_t* dst = static_cast<uint8_t*>(cache) + sl * kD;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= f32_to_e4m3(__fdiv_rn(x[i], sc)) << (8 * i);
+      hi |= f32_to_e4m3(__fdiv_rn(x[4 + i], sc)) << (8 * i);
+    }
+    *reinterpret_cast<u32x2_t*>(dst + 8 * lane) = u32x2_t{lo, hi};
+    if (lane < kDr / 2)
+      *reinterpret_cast<uint16_t*>(dst + kDc + 2 * lane) =
+          static_cast<uint16_t>(f32_to_e4m3(__fdiv_rn(y0, sc)) | (f32_to_e4m3(__fdiv_rn(y1, sc)) << 8));
+    if (lane == 0) kv_scale[sl] = sc;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // decode (generic): one workgroup per (part, head); 16-token sub-tiles staged
 // in LDS as float32; single-pass online softmax; per-segment result either
@@ -382,6 +439,18 @@ static void append_dispatch(const mla_dims& d, int32_t T_, const void* c_kv, con
 hipError_t launch_cache_append(const mla_dims& d, int32_t T_, const void* c_kv, const void* k_r,
                                const int32_t* pos, const int64_t* slot, void* cache,
                                float* kv_scale, hipStream_t s) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(c_kv) & 15u) == 0 && (reinterpret_cast<uintptr_t>(k_r) & 3u) == 0 &&
+                       (reinterpret_cast<uintptr_t>(cache) & 15u) == 0;
+  if (d.act_dtype == MLA_BF16 && d.d_latent == 512 && d.d_rope == 64 && aligned &&
+      (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_E4M3)) {
+    auto c = static_cast<const uint16_t*>(c_kv);
+    auto k = static_cast<const uint16_t*>(k_r);
+    if (d.kv_dtype == MLA_BF16)
+      cache_append_576<MLA_BF16><<<T_, 64, 0, s>>>(c, k, pos, slot, cache, kv_scale, std::log2(d.rope_base));
+    else
+      cache_append_576<MLA_E4M3><<<T_, 64, 0, s>>>(c, k, pos, slot, cache, kv_scale, std::log2(d.rope_base));
+    return hipGetLastError();
+  }
   if (d.act_dtype == MLA_F32) append_dispatch<float>(d, T_, c_kv, k_r, pos, slot, cache, kv_scale, s);
   else append_dispatch<bf16_t>(d, T_, c_kv, k_r, pos, slot, cache, kv_scale, s);
   return hipGetLastError();

@@ -234,6 +234,20 @@ __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
   return v;
 }
 
+// Maximum over the 64 lanes of a wave, returned in every lane: the DPP scan
+// pattern of wave_incl_scan with max, then lane 63 read back.
+__device__ __forceinline__ float wave_max_all(float x) {
+  int v = __float_as_int(x);
+  const int ninf = __float_as_int(-INFINITY);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(ninf, v, 0x111, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(ninf, v, 0x112, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(ninf, v, 0x114, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(ninf, v, 0x118, 0xf, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(ninf, v, 0x142, 0xa, 0xf, false))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(__builtin_amdgcn_update_dpp(ninf, v, 0x143, 0xc, 0xf, false))));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+
 // The part of the split-KV schedule one workgroup needs, in two barriers and
 // no search: the total page count P, the part's page range [x0, x1) and, when
 // the part is not empty, the sequence b owning page x0 and that sequence's
