@@ -92,15 +92,16 @@ __device__ __forceinline__ f32x16 qk_page(const LDSP char* __restrict__ ap, cons
                                           const uint32_t (&offa)[19], const char* nsrc_u, uint32_t nbuf_u,
                                           int wave) {
   f32x16 S;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) S[r] = 0.f;
   constexpr int kPre = 4;
   bf16x8 af[kPre];
 #pragma unroll
   for (int kb = 0; kb < kPre; ++kb) af[kb] = *(const LDSP bf16x8*)(ap + 32 * kb);
 #pragma unroll
   for (int kb = 0; kb < 36; ++kb) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(af[kb % kPre]), "a"(qf[kb]));
+    if (kb == 0)                                                  // accumulator starts from the constant 0
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(S) : "v"(af[0]), "a"(qf[0]));
+    else
+      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(af[kb % kPre]), "a"(qf[kb]));
     if (kb + kPre < 36) af[kb % kPre] = *(const LDSP bf16x8*)(ap + 32 * (kb + kPre));
     if (kDma && (kb & 1) == 0) dma16_u(nsrc_u, offa[kb >> 1], nbuf_u + 1024 * (wave + 4 * (kb >> 1)));
   }
@@ -373,13 +374,18 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     barrier_lds();                                               // buffer 1 free again (page 0 may still land)
 
 
-    for (int64_t jp = jp0; jp < jp1; ++jp) {
-      const bool even = ((jp - jp0) & 1) == 0;
+    // Page indices are wave-uniform 32-bit values (SGPRs): the loop control
+    // costs scalar instructions only.
+    const int32_t j0 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(jp0));
+    const int32_t j1 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(jp1));
+    const int32_t Lu = __builtin_amdgcn_readfirstlane(L);
+    for (int32_t jp = j0; jp < j1; ++jp) {
+      const bool even = ((jp - j0) & 1) == 0;
       LDSP char* buf = even ? (LDSP char*)g_page0 : (LDSP char*)g_page1;
       LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
-      const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - jp * kBs);
-      const bool more = jp + 1 < jp1;
-      page_step(ln, buf, nbuf, more, cbase, jp + 2 < jp1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
+      const int nvalid = min(kBs, Lu - jp * kBs);                 // jp * 64 < L: no overflow
+      const bool more = jp + 1 < j1;
+      page_step(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
                 nvalid, s2, acc);
     }
 
