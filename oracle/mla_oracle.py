@@ -164,6 +164,23 @@ def explicit_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, scale: float, base: floa
     return dict(out=out, o_lat=o_lat, lse=lse, weights=weights, heads=heads)
 
 
+def window_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, start: int, scale: float, base: float,
+                  k_r_rotated: bool = False, heads=None):
+    """Decode of one sequence that attends only to its rows j >= start.
+
+    ([P2] "所以 cache 逻辑到底哪里要重写": with the cache paged by token
+    latent, eviction such as a sliding window works as before.)  The rows
+    keep their absolute positions (RoPE of row j uses position j) and the
+    query stays at position L - 1; rows before ``start`` simply take no part.
+    An empty window (start >= L) gives o_lat = 0, out = 0, lse = -inf.
+    """
+    c_kv, k_r = _f64(c_kv), _f64(k_r)
+    L = c_kv.shape[0]
+    start = min(max(int(start), 0), L)
+    return explicit_decode(q_c, q_r, c_kv[start:], k_r[start:], w_uk, w_uv, scale=scale, base=base,
+                           q_pos=L - 1, k_pos=np.arange(start, L), k_r_rotated=k_r_rotated, heads=heads)
+
+
 # ----------------------------------------------------------------------------
 # Absorbed form ([P2] "第二步，推理时的吸收"; [P3] "3. 一个聪明的优化")
 # ----------------------------------------------------------------------------

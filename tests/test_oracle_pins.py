@@ -73,14 +73,14 @@ def _bf_rope(vec, p, base):
     return out
 
 
-def _bf_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale, base):
+def _bf_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale, base, start=0):
     n_h, d_h = len(q_c), len(q_c[0])
     L, d_c = len(c_kv), len(c_kv[0])
     outs, lses, olats = [], [], []
     for h in range(n_h):
         qr = _bf_rope(q_r[h], L - 1, base)
         s, vs = [], []
-        for j in range(L):
+        for j in range(start, L):
             kc = [math.fsum(w_uk[h][i][c] * c_kv[j][c] for c in range(d_c)) for i in range(d_h)]
             vs.append([math.fsum(w_uv[h][i][c] * c_kv[j][c] for c in range(d_c)) for i in range(d_h)])
             kr = _bf_rope(k_r[j], j, base)
@@ -90,8 +90,9 @@ def _bf_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale, base):
         e = [math.exp(x - m) for x in s]
         z = math.fsum(e)
         a = [x / z for x in e]
-        outs.append([math.fsum(a[j] * vs[j][i] for j in range(L)) for i in range(d_h)])
-        olats.append([math.fsum(a[j] * c_kv[j][c] for j in range(L)) for c in range(d_c)])
+        n = len(s)
+        outs.append([math.fsum(a[j] * vs[j][i] for j in range(n)) for i in range(d_h)])
+        olats.append([math.fsum(a[j] * c_kv[start + j][c] for j in range(n)) for c in range(d_c)])
         lses.append(m + math.log(z))
     return np.array(outs), np.array(olats), np.array(lses)
 
@@ -116,6 +117,60 @@ def test_brute_force_matches_oracle(n_h, d_h, d_c, d_r, L):
         np.testing.assert_allclose(res["out"], bo, rtol=0, atol=1e-13 * np.abs(bo).max())
         np.testing.assert_allclose(res["o_lat"], bl, rtol=0, atol=1e-13 * np.abs(bl).max())
         np.testing.assert_allclose(res["lse"], bs, rtol=0, atol=1e-13 * max(1, np.abs(bs).max()))
+
+
+# ---------------------------------------------------------------------------
+# Sliding window (keybo.xyz, "所以 cache 逻辑到底哪里要重写": eviction such as a
+# sliding window works as before over the latent rows)
+# ---------------------------------------------------------------------------
+def _window_case(seed, n_h=2, d_h=3, d_c=4, d_r=4, L=7):
+    rng = np.random.default_rng(200 + seed)
+    return (rng.standard_normal((n_h, d_h)), rng.standard_normal((n_h, d_r)), rng.standard_normal((L, d_c)),
+            rng.standard_normal((L, d_r)), rng.standard_normal((n_h, d_h, d_c)),
+            rng.standard_normal((n_h, d_h, d_c)))
+
+
+@pytest.mark.parametrize("start", [0, 1, 3, 6])
+def test_window_matches_brute_force(start):
+    args = _window_case(start)
+    scale, base = 1 / math.sqrt(3 + 4), 50.0
+    bo, bl, bs = _bf_decode(*[a.tolist() for a in args], scale, base, start=start)
+    res = O.window_decode(*args, start=start, scale=scale, base=base)
+    np.testing.assert_allclose(res["out"], bo, rtol=0, atol=1e-13 * np.abs(bo).max())
+    np.testing.assert_allclose(res["o_lat"], bl, rtol=0, atol=1e-13 * np.abs(bl).max())
+    np.testing.assert_allclose(res["lse"], bs, rtol=0, atol=1e-13 * max(1, np.abs(bs).max()))
+
+
+def test_window_and_its_complement_recombine_to_the_whole():
+    """Attention over rows [0, s) and over [s, L) merged by log-sum-exp equals
+    attention over all L rows (the softmax sum splits exactly)."""
+    args = _window_case(9, n_h=3, d_h=5, d_c=6, d_r=4, L=23)
+    q_c, q_r, c_kv, k_r, w_uk, w_uv = args
+    kw = dict(scale=0.3, base=1000.0)
+    full = O.explicit_decode(*args, **kw)
+    for s in (1, 10, 22):
+        a = O.explicit_decode(q_c, q_r, c_kv[:s], k_r[:s], w_uk, w_uv, q_pos=22, **kw)
+        b = O.window_decode(*args, start=s, **kw)
+        m = np.maximum(a["lse"], b["lse"])
+        wa, wb = np.exp(a["lse"] - m), np.exp(b["lse"] - m)
+        lse = m + np.log(wa + wb)
+        out = (wa[:, None] * a["out"] + wb[:, None] * b["out"]) / (wa + wb)[:, None]
+        np.testing.assert_allclose(lse, full["lse"], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(out, full["out"], rtol=0, atol=1e-12 * np.abs(full["out"]).max())
+
+
+def test_window_ignores_rows_before_it_and_empty_window():
+    args = list(_window_case(4, L=9))
+    kw = dict(scale=0.5, base=100.0)
+    ref = O.window_decode(*args, start=5, **kw)
+    args[2] = args[2].copy(); args[3] = args[3].copy()
+    args[2][:5] = 1e6
+    args[3][:5] = -1e6
+    got = O.window_decode(*args, start=5, **kw)
+    for k in ("out", "o_lat", "lse"):
+        np.testing.assert_array_equal(got[k], ref[k])
+    e = O.window_decode(*args, start=9, **kw)
+    assert np.all(e["o_lat"] == 0) and np.all(e["out"] == 0) and np.all(np.isneginf(e["lse"]))
 
 
 # ---------------------------------------------------------------------------
@@ -283,12 +338,24 @@ def _mutant_up_project_transposed(c_kv, w_h):
     return np.asarray(c_kv, float) @ w[:, ::-1].T  # wrong column order of W
 
 
+def _mutant_window_off_by_one(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, start, scale, base, **kw):
+    # (Counting positions from the window start instead of from 0 would not
+    # be a mistake: RoPE scores depend only on q_pos - k_pos.)
+    c_kv, k_r = np.asarray(c_kv, float), np.asarray(k_r, float)
+    L = c_kv.shape[0]
+    return O.explicit_decode(q_c, q_r, c_kv[start + 1:], k_r[start + 1:], w_uk, w_uv, scale=scale, base=base,
+                             q_pos=L - 1, k_pos=np.arange(start + 1, L), **kw)
+
+
 @pytest.mark.parametrize("name,mutant", [("rope", _mutant_rope_half_split),
-                                         ("up_project", _mutant_up_project_transposed)])
+                                         ("up_project", _mutant_up_project_transposed),
+                                         ("window_decode", _mutant_window_off_by_one)])
 def test_pins_catch_planted_mistakes(monkeypatch, name, mutant):
     monkeypatch.setattr(O, name, mutant)
     with pytest.raises(AssertionError):
-        if name == "rope":
+        if name == "window_decode":
+            test_window_matches_brute_force(3)
+        elif name == "rope":
             test_rope_closed_forms()
             test_brute_force_matches_oracle(2, 3, 4, 4, 6)
         else:
