@@ -169,6 +169,32 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_abs, co
                       size_t workspace_bytes, void* o_lat, float* lse, void* stream);
 
 /*
+ * mla_decode_window - mla_decode over a window of each sequence's rows.
+ *   Source: keybo.xyz page, section "所以 cache 逻辑到底哪里要重写": with the
+ *   cache paged by token latent, eviction policies such as a sliding window
+ *   or dropping tokens work as before, and several requests that share a
+ *   prefix share its latent pages.
+ *
+ *   Sequence b attends to its rows j with seq_starts[b] <= j < L (L =
+ *   seq_lens[b]); everything else is as in mla_decode, which is this call
+ *   with every start 0.  Only the block-table entries from
+ *   seq_starts[b] / block_size to ceil(L / block_size) - 1 are read, so the
+ *   pages wholly before the window may already be freed or reused (their
+ *   entries are ignored); rows of the first page that lie before the window
+ *   are read but carry weight zero, whatever they hold.  Several sequences
+ *   may name the same physical page (a shared prefix): pages are only read.
+ *   A window with seq_starts[b] >= L is empty: o_lat = 0, lse = -inf.
+ *
+ *   seq_starts  [batch]   int32, 0 <= seq_starts[b] (device memory); NULL
+ *                         means all zero
+ *   Other arguments, workspace size and errors: as mla_decode.
+ */
+mla_status mla_decode_window(const mla_dims* dims, int32_t batch, const void* q_abs, const void* kv_cache,
+                             const float* kv_scale, const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, const int32_t* seq_starts, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream);
+
+/*
  * mla_up_v - the single W_UV up-projection after the latent weighted sum.
  *   Source: keybo.xyz page, section "第二步，推理时的吸收" (output identity).
  *

@@ -117,7 +117,7 @@ struct State {                     // one wave's running state for its token blo
 // QK, softmax and PV of one page for wave w's 16 tokens (codes in `slot`).
 __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ codes, const LDSP float* __restrict__ sc,
                                              const bf16x8 (&qf)[18], int wave, int lane, int nvalid,
-                                             float s2, State& st) {
+                                             int lo, float s2, State& st) {
   const int g = lane >> 4, s = lane & 15;
   // S^T[tok 16w + 4g + r][head s]; lane (g, s) reads token row 16w + s, codes 32 ks + 8g..+7
   f32x4 S = {0.f, 0.f, 0.f, 0.f};
@@ -141,7 +141,7 @@ __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ codes
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * wave + 4 * g + r;
     scl[r] = sc[t];
-    v[r] = t < nvalid ? S[r] * s2 * scl[r] : -INFINITY;
+    v[r] = (t < nvalid && t >= lo) ? S[r] * s2 * scl[r] : -INFINITY;
     mb = fmaxf(mb, v[r]);
   }
   mb = max_xor32(max_xor16(mb));
@@ -154,9 +154,10 @@ __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ codes
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * wave + 4 * g + r;
-    const float e = t < nvalid ? __builtin_amdgcn_exp2f(v[r] - st.m_ref) : 0.f;
+    const bool ok = t < nvalid && t >= lo;
+    const float e = ok ? __builtin_amdgcn_exp2f(v[r] - st.m_ref) : 0.f;
     ps += e;
-    p[r] = t < nvalid ? e * scl[r] : 0.f;
+    p[r] = ok ? e * scl[r] : 0.f;
   }
   st.l_part = st.l_part * alpha + ps;
   if (__any(alpha != 1.f)) {
@@ -170,12 +171,15 @@ __device__ __forceinline__ void page_compute(const LDSP char* __restrict__ codes
   // V^T: in each 16-lane group g, source lane j names token row 16w + 4g +
   // (j/2 mod 4) and the 8 columns 32 c + 8 (j mod 2) + 16 (j/8); lane s then
   // receives, for tokens 16w + 4g + e, e = 0..3, column 32 c + s (first dword)
-  // and column 32 c + 16 + s (second dword).  Rows past the end of the
-  // sequence are zeroed after conversion (their codes may be anything).
+  // and column 32 c + 16 + s (second dword).  Rows outside the window (past
+  // the end of the sequence or before its start) are zeroed after conversion
+  // (their codes may be anything).
   const int jj = lane & 15;
   const LDSP char* vp = codes + (16 * wave + 4 * g + ((jj >> 1) & 3)) * kRowF + 8 * (jj & 1) + 16 * (jj >> 3);
-  const uint32_t keep01 = (16 * wave + 4 * g + 1 < nvalid) ? 0xFFFFFFFFu : (16 * wave + 4 * g < nvalid ? 0x0000FFFFu : 0u);
-  const uint32_t keep23 = (16 * wave + 4 * g + 3 < nvalid) ? 0xFFFFFFFFu : (16 * wave + 4 * g + 2 < nvalid ? 0x0000FFFFu : 0u);
+  auto keep = [&](int t) { return t >= lo && t < nvalid; };
+  const int t0 = 16 * wave + 4 * g;
+  const uint32_t keep01 = (keep(t0) ? 0x0000FFFFu : 0u) | (keep(t0 + 1) ? 0xFFFF0000u : 0u);
+  const uint32_t keep23 = (keep(t0 + 2) ? 0x0000FFFFu : 0u) | (keep(t0 + 3) ? 0xFFFF0000u : 0u);
   constexpr int kVPre = 4;
   i32x2 vf[kVPre];
 #pragma unroll
@@ -195,8 +199,8 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
     int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2,
     const uint16_t* __restrict__ q_abs, const uint8_t* __restrict__ cache, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, int32_t max_pages, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, s = lane & 15;
@@ -209,7 +213,7 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
-  const PartRange pr = locate_part(seq_lens, B, kBs, part, W, g_lens);
+  const PartRange pr = locate_part(seq_lens, seq_starts, B, kBs, part, W, g_lens);
   const int32_t chunk = pr.chunk;
   auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
   const int64_t x1 = pr.x1;
@@ -223,12 +227,17 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
   const char* cbase = reinterpret_cast<const char*>(cache);
   const int nper = page_loads(wave);
   for (;;) {
-    const int32_t L = __builtin_amdgcn_readfirstlane(seq_len(b));
-    const int64_t np = pages_of(L, kBs);
+    // The window [st0, L) of sequence b: its pages start at page fp; L and the
+    // page indices count from there; the first lo rows of that page lie
+    // before the window.
+    const int32_t st0 = __builtin_amdgcn_readfirstlane(seq_start(seq_starts, b));
+    const int32_t fp = st0 / kBs, lo = st0 - fp * kBs;
+    const int32_t L = __builtin_amdgcn_readfirstlane(seq_len(b)) - fp * kBs;
+    const int64_t np = window_pages(L + fp * kBs, st0, kBs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
     const int n = static_cast<int>(jp1 - jp0);                  // pages of this segment
-    const int32_t* bt = block_table + (int64_t)b * max_pages;
+    const int32_t* bt = block_table + (int64_t)b * max_pages + fp;
 
     // The segment's first three pages into slots 0-2, and this head group's
     // 16 query rows (18 KiB, contiguous in q_abs) into slot 3, which is free
@@ -275,7 +284,7 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
       if (i + 3 < n) issue(i + 3);
       const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - (jp0 + i) * kBs);
       page_compute((const LDSP char*)g_ring + (i & 3) * kSlotB, (const LDSP float*)g_sc[i & 3], qf, wave, lane,
-                   nvalid, s2, st);
+                   nvalid, jp0 + i == 0 ? lo : 0, s2, st);
     }
 
     // ---- merge the four waves' states, normalise, store ----------------------
@@ -324,7 +333,8 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
 
     x += jp1 - jp0;
     if (x >= x1) break;
-    do { ++b; } while (pages_of(__builtin_amdgcn_readfirstlane(seq_len(b)), kBs) == 0);
+    do { ++b; } while (window_pages(__builtin_amdgcn_readfirstlane(seq_len(b)),
+                                    __builtin_amdgcn_readfirstlane(seq_start(seq_starts, b)), kBs) == 0);
     first = x;
     __syncthreads();                                            // slots read before the next loads
   }
@@ -339,18 +349,18 @@ bool fp8_decode_supported(const mla_dims& d) {
 
 hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                              const void* cache, const float* kv_scale, const int32_t* block_table,
-                             int32_t max_pages, const int32_t* seq_lens, float* ws_o, float* ws_lse,
-                             void* o_lat, float* lse, hipStream_t s) {
+                             int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts,
+                             float* ws_o, float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
   const int HG = d.n_heads / kHeads;
   const int W = plan.parts;
   const int grid = ((W + 7) / 8) * 8 * HG;                      // 8 XCDs x ceil(W/8) parts x HG
   const float s2 = d.softmax_scale * 1.4426950408889634f;
   decode_fp8_h16<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
                                       static_cast<const uint8_t*>(cache), kv_scale, block_table, max_pages,
-                                      seq_lens, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
+                                      seq_lens, seq_starts, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_combine(d, plan, B, seq_lens, ws_o, ws_lse, o_lat, lse, s);
+  return launch_combine(d, plan, B, seq_lens, seq_starts, ws_o, ws_lse, o_lat, lse, s);
 }
 
 }  // namespace mla

@@ -142,7 +142,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
                                           LDSP char* __restrict__ nbuf,
                                           bool dma, const char* cbase, const int32_t* bt_after,
                                           int32_t& pg_after, const uint32_t (&offa)[19],
-                                          const bf16x8 (&qf)[36], int nvalid, float s2, Acc& acc) {
+                                          const bf16x8 (&qf)[36], int nvalid, int lo, float s2, Acc& acc) {
   LDSP char* pt = (LDSP char*)g_pt;
   float* xm = g_xm;
   float* xa = g_xa;
@@ -163,13 +163,14 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
                           : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
 
   // Scores stay raw (s2 > 0 commutes with the maximum); rows past the end of
-  // the sequence are -inf.  P below is exp2(S s2 - m) in one fma per score.
-  if (nvalid < kBs) {
+  // the sequence, and rows before the start of its window, are -inf.  P below
+  // is exp2(S s2 - m) in one fma per score.
+  if (nvalid < kBs || lo > 0) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ra = r >> 2;
       const int t = 32 * ln.th + 16 * (ra >> 1) + 2 * (ra & 1) + ln.hi + 4 * (r & 3);
-      if (t >= nvalid) S[r] = -INFINITY;
+      if (t >= nvalid || t < lo) S[r] = -INFINITY;
     }
   }
   float mloc = fmaxf(fmaxf(fmaxf(S[0], S[1]), fmaxf(S[2], S[3])), fmaxf(fmaxf(S[4], S[5]), fmaxf(S[6], S[7])));
@@ -202,9 +203,10 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     }
   };
   make_p();
-  if (nvalid < kBs) {                                            // rows past the end: zero the latent
-    for (int i = threadIdx.x; i < (kBs - nvalid) * 64; i += 256) {
-      const int row = nvalid + (i >> 6), ch = i & 63;
+  if (nvalid < kBs || lo > 0) {                                  // masked rows: zero the latent
+    for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 64; i += 256) {
+      const int k = i >> 6, ch = i & 63;
+      const int row = k < lo ? k : nvalid + (k - lo);
       *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   }
@@ -271,8 +273,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2,
     const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, int32_t max_pages, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
   Lane ln;
   const int tid = threadIdx.x;
   ln.lane = tid & 63;
@@ -293,7 +295,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
-  const PartRange pr = locate_part(seq_lens, B, kBs, part, W, g_lens);
+  const PartRange pr = locate_part(seq_lens, seq_starts, B, kBs, part, W, g_lens);
   const int32_t chunk = pr.chunk;
   auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
   const int64_t x1 = pr.x1;
@@ -321,11 +323,16 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   constexpr int64_t kPageBytesG = (int64_t)kBs * kD * 2;
 
   for (;;) {
-    const int32_t L = seq_len(b);
-    const int64_t np = pages_of(L, kBs);
+    // The window [st, L) of sequence b: its pages start at page fp; L and the
+    // page indices below count from there, and the first lo rows of that
+    // page lie before the window.
+    const int32_t st = seq_start(seq_starts, b);
+    const int32_t fp = st / kBs, lo = st - fp * kBs;
+    const int32_t L = seq_len(b) - fp * kBs;
+    const int64_t np = window_pages(seq_len(b), st, kBs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
-    const int32_t* bt = block_table + (int64_t)b * max_pages;
+    const int32_t* bt = block_table + (int64_t)b * max_pages + fp;
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
@@ -386,7 +393,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       const int nvalid = min(kBs, Lu - jp * kBs);                 // jp * 64 < L: no overflow
       const bool more = jp + 1 < j1;
       page_step(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
-                nvalid, s2, acc);
+                nvalid, jp == 0 ? lo : 0, s2, acc);
     }
 
     // ---- segment epilogue: normalise and store ------------------------------
@@ -444,7 +451,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 
     x += jp1 - jp0;
     if (x >= x1) break;
-    do { ++b; } while (pages_of(seq_len(b), kBs) == 0);
+    do { ++b; } while (window_pages(seq_len(b), seq_start(seq_starts, b), kBs) == 0);
     first = x;
     __syncthreads();
   }
@@ -535,13 +542,14 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
 // plain order once the search it needed was counted.)
 __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32_t W, int32_t HG,
                                                    const int32_t* __restrict__ seq_lens,
+                                                   const int32_t* __restrict__ seq_starts,
                                                    const float* __restrict__ ws_o,
                                                    const float* __restrict__ ws_lse,
                                                    uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
   const int per_seq = HG * 16;
   const int32_t b = blockIdx.x / per_seq;
   const int r = blockIdx.x % per_seq;
-  const SeqPages sp = seq_pages(seq_lens, B, kBs, b);
+  const SeqPages sp = seq_pages(seq_lens, seq_starts, B, kBs, b);
   const int64_t w0 = sp.np > 0 ? part_of_page(sp.first, sp.P, W) : 0;
   const int64_t w1 = sp.np > 0 ? part_of_page(sp.first + sp.np - 1, sp.P, W) : 0;
   combine_item(b, r / 16, r % 16, n_h, W, sp.P, sp.np, w0, w1, ws_o, ws_lse, o_lat, lse);
@@ -557,8 +565,8 @@ bool mfma_decode_supported(const mla_dims& d) {
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages,
-                              const int32_t* seq_lens, float* ws_o, float* ws_lse, void* o_lat,
-                              float* lse, hipStream_t s) {
+                              const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
+                              float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
   (void)kv_scale;
   const int HG = d.n_heads / 64;
   const int W = plan.parts;
@@ -566,10 +574,10 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
   const float s2 = d.softmax_scale * 1.4426950408889634f;
   decode_mfma_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
                                        static_cast<const uint16_t*>(cache), block_table, max_pages,
-                                       seq_lens, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
+                                       seq_lens, seq_starts, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, ws_o, ws_lse,
+  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, seq_starts, ws_o, ws_lse,
                                           static_cast<uint16_t*>(o_lat), lse);
   return hipGetLastError();
 }

@@ -187,8 +187,8 @@ __global__ void __launch_bounds__(256) decode_generic(
     int32_t B, int32_t n_h, int32_t d_c, int32_t d_R, int32_t bs, int32_t W, float scale,
     const TQ* __restrict__ q_abs, const void* __restrict__ cache, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, int32_t max_pages, const int32_t* __restrict__ seq_lens,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse, TQ* __restrict__ o_lat,
-    float* __restrict__ lse) {
+    const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o, float* __restrict__ ws_lse,
+    TQ* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ int32_t scan[257];
   __shared__ float tile[kGenRows * kGenMaxD];
   __shared__ float q[kGenMaxD];
@@ -196,7 +196,7 @@ __global__ void __launch_bounds__(256) decode_generic(
   const int w = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int D = d_c + d_R;
   int32_t chunk;
-  page_prefix(seq_lens, B, bs, scan, &chunk);
+  page_prefix(seq_lens, seq_starts, B, bs, scan, &chunk);
   const int64_t P = scan[blockDim.x];
   if (P == 0) return;
   const int64_t x1 = part_start(w + 1, P, W);
@@ -205,9 +205,13 @@ __global__ void __launch_bounds__(256) decode_generic(
   while (x < x1) {
     int32_t b;
     int64_t first;
-    locate_page(seq_lens, B, bs, scan, chunk, x, &b, &first);
-    const int32_t L = seq_lens[b];
-    const int64_t np = pages_of(L, bs);
+    locate_page(seq_lens, seq_starts, B, bs, scan, chunk, x, &b, &first);
+    // window [st, L): pages from fp = st / bs on; L and jp count from there,
+    // and the first lo rows of page fp lie before the window
+    const int32_t st = seq_start(seq_starts, b);
+    const int32_t fp = st / bs, lo = st - fp * bs;
+    const int32_t L = seq_lens[b] - fp * bs;
+    const int64_t np = window_pages(seq_lens[b], st, bs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
     __syncthreads();
@@ -217,16 +221,18 @@ __global__ void __launch_bounds__(256) decode_generic(
 #pragma unroll
     for (int k = 0; k < kCols; ++k) acc[k] = 0.f;
     for (int64_t jp = jp0; jp < jp1; ++jp) {
-      const int64_t page = block_table[(int64_t)b * max_pages + jp];
+      const int64_t page = block_table[(int64_t)b * max_pages + fp + jp];
       const int ntok = (int)min<int64_t>(bs, (int64_t)L - jp * bs);
-      for (int t0 = 0; t0 < ntok; t0 += kGenRows) {
+      const int tlo = jp == 0 ? lo : 0;                          // rows before the window: masked, zeroed
+      for (int t0 = tlo & ~(kGenRows - 1); t0 < ntok; t0 += kGenRows) {
         const int nt = min(kGenRows, ntok - t0);
         __syncthreads();
         for (int i = tid; i < nt * D; i += blockDim.x) {
           int r = i / D, e = i % D;
           int64_t sl = page * bs + t0 + r;
           float val;
-          if constexpr (KV == MLA_F32) val = static_cast<const float*>(cache)[sl * D + e];
+          if (t0 + r < tlo) val = 0.f;
+          else if constexpr (KV == MLA_F32) val = static_cast<const float*>(cache)[sl * D + e];
           else if constexpr (KV == MLA_BF16) val = bf16_to_f32(static_cast<const uint16_t*>(cache)[sl * D + e]);
           else val = e4m3_to_f32(static_cast<const uint8_t*>(cache)[sl * D + e]) * kv_scale[sl];
           tile[r * D + e] = val;
@@ -238,7 +244,7 @@ __global__ void __launch_bounds__(256) decode_generic(
           if (r < nt)
             for (int e = sub; e < D; e += 16) part += q[e] * tile[r * D + e];
           for (int off = 8; off > 0; off >>= 1) part += __shfl_xor(part, off, 16);
-          if (sub == 0) sc[r] = (r < nt) ? part * scale : -INFINITY;
+          if (sub == 0) sc[r] = (r < nt && t0 + r >= tlo) ? part * scale : -INFINITY;
         }
         __syncthreads();
         float mt = -INFINITY;
@@ -294,6 +300,7 @@ constexpr int kCombMaxSeg = 64;   // segments merged per pass (more are folded i
 template <typename TO>
 __global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int32_t d_c, int32_t bs,
                                                      int32_t W, const int32_t* __restrict__ seq_lens,
+                                                     const int32_t* __restrict__ seq_starts,
                                                      const float* __restrict__ ws_o,
                                                      const float* __restrict__ ws_lse,
                                                      TO* __restrict__ o_lat, float* __restrict__ lse) {
@@ -302,7 +309,7 @@ __global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int
   const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   int64_t pre = 0, tot = 0;
   for (int i = lane; i < B; i += 64) {
-    const int64_t np = pages_of(seq_lens[i], bs);
+    const int64_t np = window_pages(seq_lens[i], seq_start(seq_starts, i), bs);
     tot += np;
     if (i < b) pre += np;
   }
@@ -311,7 +318,7 @@ __global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int
     tot += __shfl_xor(tot, off);
   }
   const int64_t P = tot;
-  const int64_t np = pages_of(seq_lens[b], bs);
+  const int64_t np = window_pages(seq_lens[b], seq_start(seq_starts, b), bs);
   const int64_t row = (int64_t)b * n_h + h;
   if (np == 0) {
     for (int c = lane; c < d_c; c += 64) io<TO>::store(o_lat, row * d_c + c, 0.f);
@@ -457,14 +464,15 @@ hipError_t launch_cache_append(const mla_dims& d, int32_t T_, const void* c_kv, 
 }
 
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
-                          const float* ws_o, const float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
+                          const int32_t* seq_starts, const float* ws_o, const float* ws_lse, void* o_lat,
+                          float* lse, hipStream_t s) {
   dim3 grid(B, d.n_heads);
   if (d.act_dtype == MLA_F32)
     combine_kernel<float><<<grid, 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts, seq_lens,
-                                               ws_o, ws_lse, static_cast<float*>(o_lat), lse);
+                                               seq_starts, ws_o, ws_lse, static_cast<float*>(o_lat), lse);
   else
     combine_kernel<bf16_t><<<grid, 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts, seq_lens,
-                                                ws_o, ws_lse, static_cast<bf16_t*>(o_lat), lse);
+                                                seq_starts, ws_o, ws_lse, static_cast<bf16_t*>(o_lat), lse);
   return hipGetLastError();
 }
 
@@ -472,21 +480,22 @@ template <typename TQ>
 static void decode_generic_dispatch(const mla_dims& d, const DecodePlan& plan, int32_t B,
                                     const void* q_abs, const void* cache, const float* kv_scale,
                                     const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
-                                    float* ws_o, float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
+                                    const int32_t* seq_starts, float* ws_o, float* ws_lse, void* o_lat,
+                                    float* lse, hipStream_t s) {
   dim3 grid(plan.parts, d.n_heads);
   const TQ* q = static_cast<const TQ*>(q_abs);
   TQ* o = static_cast<TQ*>(o_lat);
   if (d.kv_dtype == MLA_F32)
     decode_generic<TQ, MLA_F32><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
   else if (d.kv_dtype == MLA_BF16)
     decode_generic<TQ, MLA_BF16><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
   else
     decode_generic<TQ, MLA_E4M3><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
   combine_kernel<TQ><<<dim3(B, d.n_heads), 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts,
-      seq_lens, ws_o, ws_lse, o, lse);
+      seq_lens, seq_starts, ws_o, ws_lse, o, lse);
 }
 
 static void workspace_split(const mla_dims& d, const DecodePlan& plan, int32_t B, void* ws,
@@ -516,8 +525,8 @@ DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
 
 hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                          const void* cache, const float* kv_scale, const int32_t* block_table,
-                         int32_t max_pages, const int32_t* seq_lens, void* ws, void* o_lat,
-                         float* lse, hipStream_t s) {
+                         int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts, void* ws,
+                         void* o_lat, float* lse, hipStream_t s) {
   float *ws_o, *ws_lse;
   workspace_split(d, plan, B, ws, &ws_o, &ws_lse);
   // the MFMA kernel loads 16-byte fragments and stores 8-byte groups
@@ -526,16 +535,16 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
                        (reinterpret_cast<uintptr_t>(o_lat) % 8 == 0);
   if (plan.kernel == kDecodeBf16 && aligned)
     return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
-                              ws_o, ws_lse, o_lat, lse, s);
+                              seq_starts, ws_o, ws_lse, o_lat, lse, s);
   if (plan.kernel == kDecodeFp8 && aligned && reinterpret_cast<uintptr_t>(kv_scale) % 16 == 0)
     return launch_decode_fp8(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
-                             ws_o, ws_lse, o_lat, lse, s);
+                             seq_starts, ws_o, ws_lse, o_lat, lse, s);
   if (d.act_dtype == MLA_F32)
     decode_generic_dispatch<float>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
-                                   ws_o, ws_lse, o_lat, lse, s);
+                                   seq_starts, ws_o, ws_lse, o_lat, lse, s);
   else
     decode_generic_dispatch<bf16_t>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
-                                    ws_o, ws_lse, o_lat, lse, s);
+                                    seq_starts, ws_o, ws_lse, o_lat, lse, s);
   return hipGetLastError();
 }
 

@@ -70,6 +70,14 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_abs, co
                       const float* kv_scale, const int32_t* block_table, int32_t max_pages,
                       const int32_t* seq_lens, int32_t num_splits, void* workspace,
                       size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
+  return mla_decode_window(dims, batch, q_abs, kv_cache, kv_scale, block_table, max_pages, seq_lens, nullptr,
+                           num_splits, workspace, workspace_bytes, o_lat, lse, stream);
+}
+
+mla_status mla_decode_window(const mla_dims* dims, int32_t batch, const void* q_abs, const void* kv_cache,
+                             const float* kv_scale, const int32_t* block_table, int32_t max_pages,
+                             const int32_t* seq_lens, const int32_t* seq_starts, int32_t num_splits,
+                             void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream) {
   mla_status st = check_dims(dims);
   if (st != MLA_OK) return st;
   if (batch < 1 || max_pages < 1 || num_splits < 0 || num_splits > 65536) return MLA_ERR_SHAPE;
@@ -79,7 +87,7 @@ mla_status mla_decode(const mla_dims* dims, int32_t batch, const void* q_abs, co
   const mla::DecodePlan plan = mla::plan_decode(*dims, batch, num_splits);
   if (workspace_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
   return hip_status(mla::launch_decode(*dims, plan, batch, q_abs, kv_cache, kv_scale, block_table,
-                                       max_pages, seq_lens, workspace, o_lat, lse,
+                                       max_pages, seq_lens, seq_starts, workspace, o_lat, lse,
                                        static_cast<hipStream_t>(stream)));
 }
 

@@ -175,8 +175,8 @@ __device__ __forceinline__ void sload2_i32(const int32_t* p, const int32_t* q, i
 }
 
 // ---- split-KV schedule -----------------------------------------------------
-// The batch's pages are flattened in sequence order (sequence b owns
-// ceil(L_b / block_size) consecutive pages) and cut into `parts` contiguous
+// The batch's pages are flattened in sequence order (sequence b owns the
+// pages of its window, see window_pages below) and cut into `parts` contiguous
 // ranges: part w covers [floor(w P / W), floor((w+1) P / W)).  A (part,
 // sequence) overlap is a segment; its partial result lives in slot w + b.
 __device__ __forceinline__ int64_t part_start(int64_t w, int64_t P, int64_t W) { return (w * P) / W; }
@@ -185,14 +185,25 @@ __device__ __forceinline__ int64_t part_of_page(int64_t x, int64_t P, int64_t W)
 }
 __device__ __forceinline__ int32_t pages_of(int32_t L, int32_t bs) { return (L + bs - 1) / bs; }
 
+// Sliding window: sequence b attends to its tokens [start_b, L_b) (start_b = 0
+// when seq_starts is null).  Its pages in the flattened list are the pages
+// from start_b / bs up to the one holding token L_b - 1; an empty window has
+// none.
+__device__ __forceinline__ int32_t seq_start(const int32_t* seq_starts, int32_t b) {
+  return seq_starts ? seq_starts[b] : 0;
+}
+__device__ __forceinline__ int32_t window_pages(int32_t L, int32_t start, int32_t bs) {
+  return start >= L ? 0 : pages_of(L, bs) - start / bs;
+}
+
 // Block-wide page prefix over sequences.  `scan` is __shared__ scratch of
 // blockDim.x + 1 ints (blockDim.x a multiple of 64, at most 1024).  After the
 // call scan[t] = pages of sequences before thread t's chunk
 // [t*chunk, (t+1)*chunk) and scan[blockDim.x] = total P.  With one sequence
 // per thread (chunk == 1) and lens_lds non-null, lens_lds[b] = seq_lens[b]
 // for every b < B, so later lookups need not go back to global memory.
-__device__ __forceinline__ void page_prefix(const int32_t* seq_lens, int32_t B, int32_t bs,
-                                            int32_t* scan, int32_t* chunk_out,
+__device__ __forceinline__ void page_prefix(const int32_t* seq_lens, const int32_t* seq_starts, int32_t B,
+                                            int32_t bs, int32_t* scan, int32_t* chunk_out,
                                             int32_t* lens_lds = nullptr) {
   __shared__ int32_t wave_tot[16];
   const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -201,9 +212,10 @@ __device__ __forceinline__ void page_prefix(const int32_t* seq_lens, int32_t B, 
   if (chunk == 1) {
     const int32_t L = t < B ? seq_lens[t] : 0;
     if (lens_lds && t < B) lens_lds[t] = L;
-    s = pages_of(L, bs);
+    s = t < B ? window_pages(L, seq_start(seq_starts, t), bs) : 0;
   } else {
-    for (int32_t b = t * chunk; b < min(B, (t + 1) * chunk); ++b) s += pages_of(seq_lens[b], bs);
+    for (int32_t b = t * chunk; b < min(B, (t + 1) * chunk); ++b)
+      s += window_pages(seq_lens[b], seq_start(seq_starts, b), bs);
   }
   int32_t v = s;                         // inclusive scan inside the wave
 #pragma unroll
@@ -259,8 +271,8 @@ struct PartRange {
   int64_t P, x0, x1, first;
   int32_t b, chunk;
 };
-__device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, int32_t B, int32_t bs, int64_t part,
-                                                 int64_t W, int32_t* lens_lds) {
+__device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, const int32_t* seq_starts, int32_t B,
+                                                 int32_t bs, int64_t part, int64_t W, int32_t* lens_lds) {
   __shared__ int32_t wave_tot[16];
   __shared__ int64_t owner[2];
   const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -270,9 +282,10 @@ __device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, int32_
   if (r.chunk == 1) {
     const int32_t L = t < B ? seq_lens[t] : 0;
     if (lens_lds && t < B) lens_lds[t] = L;
-    s = pages_of(L, bs);
+    s = t < B ? window_pages(L, seq_start(seq_starts, t), bs) : 0;
   } else {
-    for (int32_t b = t * r.chunk; b < min(B, (t + 1) * r.chunk); ++b) s += pages_of(seq_lens[b], bs);
+    for (int32_t b = t * r.chunk; b < min(B, (t + 1) * r.chunk); ++b)
+      s += window_pages(seq_lens[b], seq_start(seq_starts, b), bs);
   }
   const int32_t v = wave_incl_scan(s);
   if (lane == 63) wave_tot[wv] = v;
@@ -299,7 +312,7 @@ __device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, int32_
     int64_t first = owner[1];
     if (r.chunk > 1) {
       for (;;) {
-        const int32_t np = pages_of(seq_lens[b], bs);
+        const int32_t np = window_pages(seq_lens[b], seq_start(seq_starts, b), bs);
         if (r.x0 < first + np) break;
         first += np;
         ++b;
@@ -316,7 +329,8 @@ __device__ __forceinline__ PartRange locate_part(const int32_t* seq_lens, int32_
 struct SeqPages {
   int64_t P, first, np;
 };
-__device__ __forceinline__ SeqPages seq_pages(const int32_t* seq_lens, int32_t B, int32_t bs, int32_t b) {
+__device__ __forceinline__ SeqPages seq_pages(const int32_t* seq_lens, const int32_t* seq_starts, int32_t B,
+                                              int32_t bs, int32_t b) {
   __shared__ int32_t wave_tot[16];
   __shared__ int64_t found[2];
   const int nt = blockDim.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
@@ -324,7 +338,7 @@ __device__ __forceinline__ SeqPages seq_pages(const int32_t* seq_lens, int32_t B
   const int32_t b0 = t * chunk, b1 = min(B, b0 + chunk);
   int32_t s = 0, before = 0, mine = 0;                 // pages of the chunk, of its part before b, of b
   for (int32_t i = b0; i < b1; ++i) {
-    const int32_t np = pages_of(seq_lens[i], bs);
+    const int32_t np = window_pages(seq_lens[i], seq_start(seq_starts, i), bs);
     before += i < b ? np : 0;
     mine += i == b ? np : 0;
     s += np;
@@ -351,8 +365,8 @@ __device__ __forceinline__ SeqPages seq_pages(const int32_t* seq_lens, int32_t B
 }
 
 // Sequence owning flattened page x (0 <= x < P), and that sequence's first page.
-__device__ __forceinline__ void locate_page(const int32_t* seq_lens, int32_t B, int32_t bs,
-                                            const int32_t* scan, int32_t chunk, int64_t x,
+__device__ __forceinline__ void locate_page(const int32_t* seq_lens, const int32_t* seq_starts, int32_t B,
+                                            int32_t bs, const int32_t* scan, int32_t chunk, int64_t x,
                                             int32_t* b_out, int64_t* first_out) {
   int lo = 0, hi = blockDim.x;            // scan[lo] <= x < scan[hi]
   while (hi - lo > 1) {
@@ -367,7 +381,7 @@ __device__ __forceinline__ void locate_page(const int32_t* seq_lens, int32_t B, 
   int64_t first = scan[lo];
   int32_t b = lo * chunk;
   for (;;) {
-    int32_t np = pages_of(seq_lens[b], bs);
+    int32_t np = window_pages(seq_lens[b], seq_start(seq_starts, b), bs);
     if (x < first + np) break;
     first += np;
     ++b;

@@ -26,13 +26,14 @@ hipError_t launch_cache_append(const mla_dims& d, int32_t T, const void* c_kv, c
                                float* kv_scale, hipStream_t s);
 hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                          const void* cache, const float* kv_scale, const int32_t* block_table,
-                         int32_t max_pages, const int32_t* seq_lens, void* ws, void* o_lat,
-                         float* lse, hipStream_t s);
+                         int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts, void* ws,
+                         void* o_lat, float* lse, hipStream_t s);
 hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                        hipStream_t s);
 
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
-                          const float* ws_o, const float* ws_lse, void* o_lat, float* lse, hipStream_t s);
+                          const int32_t* seq_starts, const float* ws_o, const float* ws_lse, void* o_lat,
+                          float* lse, hipStream_t s);
 
 // MFMA projections (bf16); *handled = false when the shapes or alignments are
 // not covered, and the caller then runs the generic kernel.
@@ -48,12 +49,12 @@ bool mfma_decode_supported(const mla_dims& d);
 bool fp8_decode_supported(const mla_dims& d);
 hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                              const void* cache, const float* kv_scale, const int32_t* block_table,
-                             int32_t max_pages, const int32_t* seq_lens, float* ws_o, float* ws_lse,
-                             void* o_lat, float* lse, hipStream_t s);
+                             int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts,
+                             float* ws_o, float* ws_lse, void* o_lat, float* lse, hipStream_t s);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages,
-                              const int32_t* seq_lens, float* ws_o, float* ws_lse, void* o_lat,
-                              float* lse, hipStream_t s);
+                              const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
+                              float* ws_lse, void* o_lat, float* lse, hipStream_t s);
 
 }  // namespace mla

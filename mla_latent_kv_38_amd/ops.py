@@ -95,8 +95,10 @@ def decode_workspace_bytes(d: Dims, batch: int, num_splits: int = 0) -> int:
 
 
 def decode(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_splits: int = 0,
-           workspace=None, o_lat=None, lse=None, stream=None):
-    """Absorbed attention over the paged latent cache; returns (o_lat, lse)."""
+           workspace=None, o_lat=None, lse=None, stream=None, seq_starts=None):
+    """Absorbed attention over the paged latent cache; returns (o_lat, lse).
+    With seq_starts, sequence b attends only to its rows [seq_starts[b], L_b)
+    (mla_decode_window)."""
     at = _TORCH[d.act_dtype]
     B = q_abs.shape[0]
     D = d.d_latent + d.d_rope
@@ -106,6 +108,8 @@ def decode(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_s
     if block_table.dim() != 2 or block_table.shape[0] != B:
         raise ValueError("block_table must be [batch, max_pages]")
     _need(seq_lens, "seq_lens", torch.int32, (B,))
+    if seq_starts is not None:
+        _need(seq_starts, "seq_starts", torch.int32, (B,))
     if d.kv_dtype == MLA_E4M3:
         _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
     need = decode_workspace_bytes(d, B, num_splits)
@@ -117,10 +121,17 @@ def decode(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_s
     if lse is None:
         lse = torch.empty((B, d.n_heads), dtype=torch.float32, device=q_abs.device)
     _need(lse, "lse", torch.float32, (B, d.n_heads))
-    check(_lib.lib().mla_decode(ctypes.byref(d), B, _ptr(q_abs), _ptr(kv_cache), _ptr(kv_scale),
-                                _ptr(block_table), block_table.shape[1], _ptr(seq_lens), num_splits,
-                                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _ptr(o_lat), _ptr(lse), _stream(stream)), "mla_decode")
+    if seq_starts is None:
+        check(_lib.lib().mla_decode(ctypes.byref(d), B, _ptr(q_abs), _ptr(kv_cache), _ptr(kv_scale),
+                                    _ptr(block_table), block_table.shape[1], _ptr(seq_lens), num_splits,
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                    _ptr(o_lat), _ptr(lse), _stream(stream)), "mla_decode")
+    else:
+        check(_lib.lib().mla_decode_window(ctypes.byref(d), B, _ptr(q_abs), _ptr(kv_cache), _ptr(kv_scale),
+                                           _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                           _ptr(seq_starts), num_splits, _ptr(workspace),
+                                           workspace.numel() * workspace.element_size(), _ptr(o_lat),
+                                           _ptr(lse), _stream(stream)), "mla_decode_window")
     return o_lat, lse
 
 
