@@ -209,6 +209,22 @@ def cache_rows(c_kv, k_r_raw, pos, base: float):
     return np.concatenate([_f64(c_kv), rope(k_r_raw, _f64(pos), base)], axis=-1)
 
 
+def projected_rows(h, w_dkv, w_kr, pos, base: float, act: str):
+    """Cache rows of new tokens straight from their hidden states.
+
+    ([P2] "第一步，训练时": c_kv = W_DKV x, only the latent is cached; [P2]
+    "RoPE 为什么必须解耦": k_R = RoPE(W_KR x), rotated before caching.)  The
+    projections are stored in the activation type before they are appended,
+    so each is rounded once to ``act`` ("f32" or "bf16"); the row is then
+    [c_kv || RoPE(k_R, pos)] as in ``cache_rows``.
+    """
+    rnd = to_bf16 if act == "bf16" else to_f32
+    h = _f64(h)
+    c_kv = rnd(h @ _f64(w_dkv).T).astype(np.float64)
+    k_r = rnd(h @ _f64(w_kr).T).astype(np.float64) if np.asarray(w_kr).size else np.zeros((h.shape[0], 0))
+    return cache_rows(c_kv, k_r, pos, base)
+
+
 def latent_decode(q_abs, rows, d_c: int, scale: float):
     """Attention of absorbed queries over latent rows, as plainly defined.
 

@@ -174,6 +174,43 @@ def test_window_ignores_rows_before_it_and_empty_window():
 
 
 # ---------------------------------------------------------------------------
+# Rows straight from hidden states (keybo.xyz "第一步，训练时" and "RoPE 为什么必须解耦")
+# ---------------------------------------------------------------------------
+def test_projected_rows_of_unit_hidden_states_are_weight_columns():
+    """h = e_k (exact in bf16): the latent is column k of W_DKV and the RoPE
+    part is column k of W_KR rotated by the token's position (scalar RoPE)."""
+    rng = np.random.default_rng(12)
+    dm, d_c, d_r = 24, 8, 6
+    w_dkv = O.to_bf16(rng.standard_normal((d_c, dm))).astype(float)
+    w_kr = O.to_bf16(rng.standard_normal((d_r, dm))).astype(float)
+    ks = [0, 5, 23]
+    pos = np.array([0, 7, 130])
+    h = np.zeros((3, dm))
+    h[np.arange(3), ks] = 1.0
+    rows = O.projected_rows(h, w_dkv, w_kr, pos, 500.0, "bf16")
+    for i, k in enumerate(ks):
+        np.testing.assert_array_equal(rows[i, :d_c], w_dkv[:, k])
+        np.testing.assert_allclose(rows[i, d_c:], _bf_rope(list(w_kr[:, k]), int(pos[i]), 500.0), rtol=0, atol=1e-12)
+
+
+def test_projected_rows_round_each_projection_once():
+    """2 h gives exactly twice the bf16 latent of h (scaling by 2 commutes with
+    rounding), and an f32 latent differs from the exact product by at most
+    half an f32 ulp."""
+    rng = np.random.default_rng(13)
+    dm = 40
+    h = rng.standard_normal((4, dm))
+    w_dkv, w_kr = rng.standard_normal((16, dm)), rng.standard_normal((4, dm))
+    pos = np.arange(4)
+    a = O.projected_rows(h, w_dkv, w_kr, pos, 100.0, "bf16")
+    b = O.projected_rows(2 * h, w_dkv, w_kr, pos, 100.0, "bf16")
+    np.testing.assert_array_equal(b[:, :16], 2 * a[:, :16])
+    f = O.projected_rows(h, w_dkv, w_kr, pos, 100.0, "f32")[:, :16]
+    exact = h @ w_dkv.T
+    assert np.all(np.abs(f - exact) <= np.abs(exact) * 2.0 ** -24)
+
+
+# ---------------------------------------------------------------------------
 # Absorption identity (keybo.xyz, "第二步，推理时的吸收")
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("seed", [0, 1, 2])
