@@ -124,6 +124,40 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t n_tokens, const void* 
                             int64_t num_pages, void* kv_cache, float* kv_scale, void* stream);
 
 /*
+ * mla_kv_project_workspace_bytes - device workspace mla_kv_project_append
+ * needs for n_tokens tokens of width d_model.  Pure host computation;
+ * returns 0 when the arguments are invalid.
+ */
+size_t mla_kv_project_workspace_bytes(const mla_dims* dims, int32_t n_tokens, int32_t d_model);
+
+/*
+ * mla_kv_project_append - the down-projection of new tokens fused with their
+ * append: the latent and the RoPE key are computed from the hidden states
+ * and written straight into the paged cache.
+ *   Source: keybo.xyz page, section "第一步，训练时" (c_kv = W_DKV x; only the
+ *   latent is cached) and section "RoPE 为什么必须解耦" (k_R = RoPE(W_KR x),
+ *   rotated before it is cached); dgblog.top page, section "1. 下采样（压缩）".
+ *
+ *   c_kv[t,:] = W_DKV h[t,:],  k_r[t,:] = W_KR h[t,:]   (float32 accumulation,
+ *   each result rounded once to act_dtype, nearest-even), then exactly
+ *   mla_cache_append(c_kv, k_r, pos, slot): the result is the same as
+ *   projecting into act_dtype buffers and appending them.
+ *
+ *   h         [n_tokens, d_model]     act_dtype hidden states
+ *   w_dkv     [d_c, d_model]          act_dtype
+ *   w_kr      [d_R, d_model]          act_dtype; may be NULL if d_R = 0
+ *   pos, slot, num_pages, kv_cache, kv_scale: as mla_cache_append
+ *   workspace >= mla_kv_project_workspace_bytes(dims, n_tokens, d_model)
+ *             bytes, device memory, 256-byte aligned; clobbered
+ *   n_tokens = 0 is a no-op.  1 <= d_model <= 2^20.
+ *   Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_WORKSPACE.
+ */
+mla_status mla_kv_project_append(const mla_dims* dims, int32_t n_tokens, int32_t d_model, const void* h,
+                                 const void* w_dkv, const void* w_kr, const int32_t* pos, const int64_t* slot,
+                                 int64_t num_pages, void* kv_cache, float* kv_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
  * mla_decode_workspace_bytes - device workspace mla_decode needs for this
  * batch and split count (num_splits = 0 means the automatic choice).  Pure
  * host computation; returns 0 when the arguments are invalid.

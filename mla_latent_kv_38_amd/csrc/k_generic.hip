@@ -128,50 +128,11 @@ __global__ void __launch_bounds__(64) cache_append_576(const uint16_t* __restric
                                                        const int64_t* __restrict__ slot,
                                                        void* __restrict__ cache,
                                                        float* __restrict__ kv_scale, double log2_base) {
-  typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
-  typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-  constexpr int kDc = 512, kDr = 64, kD = 576;
   const int t = blockIdx.x, lane = threadIdx.x;
-  const u32x4_t c = *reinterpret_cast<const u32x4_t*>(c_kv + (int64_t)t * kDc + 8 * lane);
+  const u32x4_t c = *reinterpret_cast<const u32x4_t*>(c_kv + (int64_t)t * 512 + 8 * lane);
   uint32_t kp = 0;
-  if (lane < kDr / 2) kp = *reinterpret_cast<const uint32_t*>(k_r + (int64_t)t * kDr + 2 * lane);
-  const int32_t p = pos[t];
-  const int64_t sl = slot[t];
-  float y0 = 0.f, y1 = 0.f;
-  if (lane < kDr / 2)
-    rope_pair(bf16_to_f32(static_cast<uint16_t>(kp & 0xFFFFu)), bf16_to_f32(static_cast<uint16_t>(kp >> 16)), p, lane,
-              kDr, log2_base, &y0, &y1);
-  if constexpr (KV == MLA_BF16) {
-    uint16_t* dst = static_cast<uint16_t*>(cache) + sl * kD;
-    *reinterpret_cast<u32x4_t*>(dst + 8 * lane) = c;
-    if (lane < kDr / 2)
-      *reinterpret_cast<uint32_t*>(dst + kDc + 2 * lane) =
-          static_cast<uint32_t>(f32_to_bf16(y0)) | (static_cast<uint32_t>(f32_to_bf16(y1)) << 16);
-  } else {
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[2 * i] = __uint_as_float(c[i] << 16);
-      x[2 * i + 1] = __uint_as_float(c[i] & 0xFFFF0000u);
-    }
-    float amax = fmaxf(fabsf(y0), fabsf(y1));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
-    amax = wave_max_all(amax);
-    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
-    uint8_t* dst = static_cast<uint8_t*>(cache) + sl * kD;
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lo |= f32_to_e4m3(__fdiv_rn(x[i], sc)) << (8 * i);
-      hi |= f32_to_e4m3(__fdiv_rn(x[4 + i], sc)) << (8 * i);
-    }
-    *reinterpret_cast<u32x2_t*>(dst + 8 * lane) = u32x2_t{lo, hi};
-    if (lane < kDr / 2)
-      *reinterpret_cast<uint16_t*>(dst + kDc + 2 * lane) =
-          static_cast<uint16_t>(f32_to_e4m3(__fdiv_rn(y0, sc)) | (f32_to_e4m3(__fdiv_rn(y1, sc)) << 8));
-    if (lane == 0) kv_scale[sl] = sc;
-  }
+  if (lane < 32) kp = *reinterpret_cast<const uint32_t*>(k_r + (int64_t)t * 64 + 2 * lane);
+  append_row_576<KV == MLA_E4M3>(c, kp, pos[t], slot[t], cache, kv_scale, log2_base, lane);
 }
 
 // ---------------------------------------------------------------------------

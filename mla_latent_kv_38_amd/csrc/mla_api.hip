@@ -10,6 +10,7 @@ namespace {
 thread_local int32_t g_last_hip_error = 0;
 
 constexpr int32_t kMaxWidth = 1024;   // d_head, d_latent + d_rope limit of the generic kernels
+constexpr int32_t kMaxModel = 1 << 20; // d_model limit of the fused projection
 
 bool valid_dtype(int32_t t, bool allow_e4m3) {
   return t == MLA_F32 || t == MLA_BF16 || (allow_e4m3 && t == MLA_E4M3);
@@ -98,6 +99,29 @@ mla_status mla_up_v(const mla_dims* dims, int32_t batch, const void* o_lat, cons
   if (batch < 1) return MLA_ERR_SHAPE;
   if (!o_lat || !w_uv || !out) return MLA_ERR_NULL;
   return hip_status(mla::launch_up_v(*dims, batch, o_lat, w_uv, out, static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_kv_project_workspace_bytes(const mla_dims* dims, int32_t n_tokens, int32_t d_model) {
+  if (check_dims(dims) != MLA_OK || n_tokens < 0 || d_model < 1 || d_model > kMaxModel) return 0;
+  return mla::kv_project_workspace_bytes(*dims, n_tokens, d_model);
+}
+
+mla_status mla_kv_project_append(const mla_dims* dims, int32_t n_tokens, int32_t d_model, const void* h,
+                                 const void* w_dkv, const void* w_kr, const int32_t* pos, const int64_t* slot,
+                                 int64_t num_pages, void* kv_cache, float* kv_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (n_tokens < 0 || num_pages < 1 || d_model < 1 || d_model > kMaxModel) return MLA_ERR_SHAPE;
+  if (n_tokens == 0) return MLA_OK;
+  if (!h || !w_dkv || !pos || !slot || !kv_cache || !workspace || (dims->d_rope > 0 && !w_kr))
+    return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0 ||
+      workspace_bytes < mla::kv_project_workspace_bytes(*dims, n_tokens, d_model))
+    return MLA_ERR_WORKSPACE;
+  return hip_status(mla::launch_kv_project_append(*dims, n_tokens, d_model, h, w_dkv, w_kr, pos, slot, kv_cache,
+                                                  kv_scale, workspace, static_cast<hipStream_t>(stream)));
 }
 
 const char* mla_status_string(mla_status s) {

@@ -260,6 +260,55 @@ __device__ __forceinline__ float wave_max_all(float x) {
   return __int_as_float(__builtin_amdgcn_readlane(v, 63));
 }
 
+// One 576-wide cache row (d_c = 512, d_R = 64) from bfloat16 inputs, written
+// by one wave: lane l holds latent elements 8l..8l+7 (c, bf16 bits) and, for
+// l < 32, the unrotated RoPE pair l (kp, two bf16).  A bf16 cache receives
+// the latent bits unchanged (bf16 -> float -> bf16 is exact) and the rotated
+// pair rounded once; an E4M3 cache receives e4m3(x / s) with s = amax / 448
+// over the whole row (1 for an all-zero row), s stored in kv_scale[slot].
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+template <bool kE4M3>
+__device__ __forceinline__ void append_row_576(u32x4_t c, uint32_t kp, int32_t p, int64_t sl, void* cache,
+                                               float* kv_scale, double log2_base, int lane) {
+  constexpr int kDc = 512, kDr = 64, kD = 576;
+  float y0 = 0.f, y1 = 0.f;
+  if (lane < kDr / 2)
+    rope_pair(bf16_to_f32(static_cast<uint16_t>(kp & 0xFFFFu)), bf16_to_f32(static_cast<uint16_t>(kp >> 16)), p, lane,
+              kDr, log2_base, &y0, &y1);
+  if constexpr (!kE4M3) {
+    uint16_t* dst = static_cast<uint16_t*>(cache) + sl * kD;
+    *reinterpret_cast<u32x4_t*>(dst + 8 * lane) = c;
+    if (lane < kDr / 2)
+      *reinterpret_cast<uint32_t*>(dst + kDc + 2 * lane) =
+          static_cast<uint32_t>(f32_to_bf16(y0)) | (static_cast<uint32_t>(f32_to_bf16(y1)) << 16);
+  } else {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(c[i] << 16);
+      x[2 * i + 1] = __uint_as_float(c[i] & 0xFFFF0000u);
+    }
+    float amax = fmaxf(fabsf(y0), fabsf(y1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+    amax = wave_max_all(amax);
+    const float sc = amax > 0.f ? __fdiv_rn(amax, 448.0f) : 1.0f;
+    uint8_t* dst = static_cast<uint8_t*>(cache) + sl * kD;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lo |= f32_to_e4m3(__fdiv_rn(x[i], sc)) << (8 * i);
+      hi |= f32_to_e4m3(__fdiv_rn(x[4 + i], sc)) << (8 * i);
+    }
+    *reinterpret_cast<u32x2_t*>(dst + 8 * lane) = u32x2_t{lo, hi};
+    if (lane < kDr / 2)
+      *reinterpret_cast<uint16_t*>(dst + kDc + 2 * lane) =
+          static_cast<uint16_t>(f32_to_e4m3(__fdiv_rn(y0, sc)) | (f32_to_e4m3(__fdiv_rn(y1, sc)) << 8));
+    if (lane == 0) kv_scale[sl] = sc;
+  }
+}
+
 // The part of the split-KV schedule one workgroup needs, in two barriers and
 // no search: the total page count P, the part's page range [x0, x1) and, when
 // the part is not empty, the sequence b owning page x0 and that sequence's

@@ -31,6 +31,11 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
 hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                        hipStream_t s);
 
+size_t kv_project_workspace_bytes(const mla_dims& d, int32_t T, int32_t dm);
+hipError_t launch_kv_project_append(const mla_dims& d, int32_t T, int32_t dm, const void* h, const void* w_dkv,
+                                    const void* w_kr, const int32_t* pos, const int64_t* slot, void* cache,
+                                    float* kv_scale, void* ws, hipStream_t s);
+
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
                           const int32_t* seq_starts, const float* ws_o, const float* ws_lse, void* o_lat,
                           float* lse, hipStream_t s);

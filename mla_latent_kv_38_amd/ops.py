@@ -90,6 +90,36 @@ def cache_append(d: Dims, c_kv, k_r, pos, slot, kv_cache, kv_scale=None, stream=
           "mla_cache_append")
 
 
+def kv_project_workspace_bytes(d: Dims, n_tokens: int, d_model: int) -> int:
+    return int(_lib.lib().mla_kv_project_workspace_bytes(ctypes.byref(d), n_tokens, d_model))
+
+
+def kv_project_append(d: Dims, h, w_dkv, w_kr, pos, slot, kv_cache, kv_scale=None, workspace=None,
+                      stream=None):
+    """c_kv = W_DKV h, k_R = W_KR h (rounded to the activation type), appended
+    as [c_kv || RoPE(k_R, pos)] rows at the given slots."""
+    at = _TORCH[d.act_dtype]
+    T, dm = h.shape
+    _need(h, "h", at, (T, dm))
+    _need(w_dkv, "w_dkv", at, (d.d_latent, dm))
+    if d.d_rope:
+        _need(w_kr, "w_kr", at, (d.d_rope, dm))
+    _need(pos, "pos", torch.int32, (T,))
+    _need(slot, "slot", torch.int64, (T,))
+    _need(kv_cache, "kv_cache", _kv_torch(d))
+    if kv_cache.dim() != 3 or kv_cache.shape[1] != d.block_size or kv_cache.shape[2] != d.d_latent + d.d_rope:
+        raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)}")
+    if d.kv_dtype == MLA_E4M3:
+        _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    need = kv_project_workspace_bytes(d, T, dm)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
+    check(_lib.lib().mla_kv_project_append(ctypes.byref(d), T, dm, _ptr(h), _ptr(w_dkv), _ptr(w_kr), _ptr(pos),
+                                           _ptr(slot), kv_cache.shape[0], _ptr(kv_cache), _ptr(kv_scale),
+                                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                           _stream(stream)), "mla_kv_project_append")
+
+
 def decode_workspace_bytes(d: Dims, batch: int, num_splits: int = 0) -> int:
     return int(_lib.lib().mla_decode_workspace_bytes(ctypes.byref(d), batch, num_splits))
 

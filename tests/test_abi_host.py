@@ -95,6 +95,26 @@ def test_validation_errors_launch_nothing():
     assert lib.mla_decode(ref(d8), 16, *args, ws, 1 << 40, FAKE, NULL, NULL) == -1   # no kv_scale
     args_bad_split = [FAKE, FAKE, NULL, FAKE, 64, FAKE, 70000]
     assert lib.mla_decode(ref(d), 16, *args_bad_split, ws, 1 << 40, FAKE, NULL, NULL) == -2
+    # decode_window: same validation as decode; seq_starts may be NULL
+    assert lib.mla_decode_window(ref(d), 16, FAKE, FAKE, NULL, FAKE, 64, FAKE, FAKE, 0, ws, need - 1,
+                                 FAKE, NULL, NULL) == -4
+    assert lib.mla_decode_window(ref(d), 16, FAKE, FAKE, NULL, FAKE, 64, NULL, FAKE, 0, ws, need,
+                                 FAKE, NULL, NULL) == -1
+    assert lib.mla_decode_window(ref(d), 16, FAKE, FAKE, NULL, FAKE, 0, FAKE, NULL, 0, ws, need,
+                                 FAKE, NULL, NULL) == -2
+    # kv_project_append
+    pw = lib.mla_kv_project_workspace_bytes(ref(d), 16, 5120)
+    assert pw >= 16 * 576 * 4
+    assert lib.mla_kv_project_workspace_bytes(ref(d), 16, 0) == 0
+    assert lib.mla_kv_project_workspace_bytes(ref(d), -1, 5120) == 0
+    pargs = [FAKE, FAKE, FAKE, FAKE, FAKE, 1, FAKE, NULL]
+    assert lib.mla_kv_project_append(ref(d), 0, 5120, *[NULL] * 5, 1, NULL, NULL, NULL, 0, NULL) == 0  # no-op
+    assert lib.mla_kv_project_append(ref(d), 16, 5120, *pargs, ws, pw - 1, NULL) == -4
+    assert lib.mla_kv_project_append(ref(d), 16, 5120, *pargs, ctypes.c_void_p(0x10010), pw, NULL) == -4
+    assert lib.mla_kv_project_append(ref(d), 16, 0, *pargs, ws, pw, NULL) == -2
+    assert lib.mla_kv_project_append(ref(d), 16, 5120, FAKE, FAKE, NULL, FAKE, FAKE, 1, FAKE, NULL, ws, pw,
+                                     NULL) == -1                                   # no W_KR with d_R > 0
+    assert lib.mla_kv_project_append(ref(d8), 16, 5120, *pargs, ws, 1 << 40, NULL) == -1   # no kv_scale
     # up_v
     assert lib.mla_up_v(ref(d), 16, FAKE, NULL, FAKE, NULL) == -1
     assert lib.mla_up_v(ref(d), -3, FAKE, FAKE, FAKE, NULL) == -2
