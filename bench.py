@@ -215,6 +215,8 @@ def main():
     if dec_us is None:                   # graph replay: the decode call is timed in the eager pass
         dec_us = call_us["decode"]
 
+    kvp = kv_project_measure(mla, d, w, dev, B, args.min_replica_mb)
+
     # algorithmic work of one decode call
     toks = int(w.lens.sum())
     kv_bytes = toks * row_bytes
@@ -256,11 +258,66 @@ def main():
         "call_us": {k: round(v, 3) for k, v in call_us.items()},
         "roofline": roof,
         "cache_fill_GBps": round(cache_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
+        "kv_project": kvp,
     }
 
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, row_bytes)
     print(json.dumps(res))
+
+
+def kv_project_measure(mla, d, w, dev, T, min_mb, d_model=5120, iters=50):
+    """mla_kv_project_append for the step's T new tokens (d_model = 5120, the
+    DeepSeek-V2 hidden width): mean call time over calls that rotate through
+    enough copies of W_DKV / W_KR (random, bf16) to exceed the MALL, replayed
+    from a captured graph, and its HBM rate on the algorithmic bytes (weights
+    once, hidden states, rows written)."""
+    import torch
+    if w.act != "bf16":
+        return None
+    wb = (w.d_c + w.d_R) * d_model * 2
+    R = max(1, math.ceil(min_mb * 1e6 / wb))
+    gen = torch.Generator(device=dev).manual_seed(7)
+    mk = lambda r, c: (torch.randn((r, c), generator=gen, device=dev) / math.sqrt(c)).to(torch.bfloat16)
+    ws_w = [(mk(w.d_c, d_model), mk(w.d_R, d_model)) for _ in range(R)]
+    h = torch.randn((T, d_model), generator=gen, device=dev).to(torch.bfloat16)
+    pages = (T + w.block_size - 1) // w.block_size
+    if w.kv == "e4m3":
+        cache = torch.zeros((pages, w.block_size, w.D), dtype=torch.uint8, device=dev)
+        scale = torch.ones((pages, w.block_size), dtype=torch.float32, device=dev)
+    else:
+        cache = torch.zeros((pages, w.block_size, w.D), dtype=torch.bfloat16, device=dev)
+        scale = None
+    pos = torch.arange(T, dtype=torch.int32, device=dev)
+    slot = torch.arange(T, dtype=torch.int64, device=dev)
+    ws = torch.empty(mla.kv_project_workspace_bytes(d, T, d_model), dtype=torch.uint8, device=dev)
+    for i in range(5):
+        mla.kv_project_append(d, h, *ws_w[i % R], pos, slot, cache, scale, workspace=ws)
+    torch.cuda.synchronize()
+    # one captured graph calls it once per weight copy, so the timing is the
+    # device's (two kernels per call), not the Python loop's
+    gph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gph):
+        for i in range(R):
+            mla.kv_project_append(d, h, *ws_w[i], pos, slot, cache, scale, workspace=ws)
+    gph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(1, iters // R + 1)
+    e0.record(stream)
+    for _ in range(reps):
+        gph.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (reps * R) * 1e3
+    esz = 1 if w.kv == "e4m3" else 2
+    nbytes = wb + T * d_model * 2 + T * (w.D * esz + (4 if w.kv == "e4m3" else 0))
+    gbps = nbytes / (us * 1e-6) / 1e9
+    del ws_w
+    return {"tokens": T, "d_model": d_model, "us": round(us, 3), "algorithmic_bytes": nbytes,
+            "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "weight_copies": R,
+            "launch": "graph"}
 
 
 def cpu_baseline(w, nseq, row_bytes):

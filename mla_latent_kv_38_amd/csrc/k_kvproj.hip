@@ -13,7 +13,7 @@
 // else), so it is cut into 36 blocks of 16 output features x KS slices of
 // d_model, one wave each, on v_mfma_f32_16x16x32_bf16 with the weight as the
 // A operand and the tokens as B; each wave stores float32 partial sums.  The
-// second kernel (one wave per token) adds the KS partials, rounds to bf16 and
+// second kernel (one workgroup per token) adds the KS partials, rounds to bf16 and
 // writes the row with the same code as the 576-wide append.  Any other shape
 // or alignment: one workgroup per token computes the rounded c_kv and k_R into
 // the workspace and the ordinary append kernel writes them.
@@ -34,47 +34,88 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kRow = 576;                       // d_c + d_R of the MFMA path
 constexpr int kFeatBlocks = kRow / 16;          // 36
-constexpr int kTargetWaves = 512;               // slices chosen so the grid has about this many waves
+constexpr int kSliceSteps = 8;                  // 32-wide k-steps per slice: 20 slices (720 waves) at d_model 5120
 
-// part[j][t][f] = sum over k in slice j of W[f][k] h[t][k], f < 512 from
-// W_DKV, f >= 512 from W_KR.  Grid (36, KS), one wave; kc is a multiple of 32.
-__global__ void __launch_bounds__(64) kv_proj_partial(int32_t T, int32_t dm, int32_t kc,
-                                                      const uint16_t* __restrict__ h,
+// part[j][t][f] = sum over k in slice j (kSteps x 32 wide) of W[f][k] h[t][k],
+// f < 512 from W_DKV, f >= 512 from W_KR.  Grid (36, slices), one wave.  All
+// of the slice's weight fragments are loaded before the first MFMA (they
+// stay in registers for every 16-token block), and each block's token
+// fragments likewise, so a wave waits for memory once per block.
+template <int kSteps>
+__global__ void __launch_bounds__(64) kv_proj_partial(int32_t T, int32_t dm, const uint16_t* __restrict__ h,
                                                       const uint16_t* __restrict__ w_dkv,
                                                       const uint16_t* __restrict__ w_kr,
                                                       float* __restrict__ part) {
   const int lane = threadIdx.x, g = lane >> 4, s = lane & 15;
   const int f0 = 16 * blockIdx.x, f = f0 + s;
   const uint16_t* wrow = f < 512 ? w_dkv + (int64_t)f * dm : w_kr + (int64_t)(f - 512) * dm;
-  const int k0 = blockIdx.y * kc, k1 = min(dm, k0 + kc);
+  const int k0 = blockIdx.y * (32 * kSteps);
+  bf16x8 a[kSteps];
+#pragma unroll
+  for (int i = 0; i < kSteps; ++i) {
+    const int k = k0 + 32 * i;
+    a[i] = k < dm ? *reinterpret_cast<const bf16x8*>(wrow + k + 8 * g) : bf16x8{};
+  }
   for (int tb = 0; tb < T; tb += 16) {
     const uint16_t* hrow = h + (int64_t)min(tb + s, T - 1) * dm;   // rows past T: read a real row, not stored
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int k = k0; k < k1; k += 32) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(wrow + k + 8 * g);
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(hrow + k + 8 * g);
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    bf16x8 b[kSteps];
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) {
+      const int k = k0 + 32 * i;
+      b[i] = k < dm ? *reinterpret_cast<const bf16x8*>(hrow + k + 8 * g) : bf16x8{};
     }
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kSteps; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[i], acc, 0, 0, 0);
     if (tb + s < T)                                  // D[4g + r][s]: features f0 + 4g + r of token tb + s
       *reinterpret_cast<f32x4*>(part + ((int64_t)blockIdx.y * T + tb + s) * kRow + f0 + 4 * g) = acc;
   }
 }
 
 // Sum of the KS partials of token t, rounded to bf16, then the cache row.
+// Four waves per token: wave w adds slices w, w + 4, ... (up to kPerWave of
+// them, all loads in flight together), the four sums meet in LDS and wave 0
+// writes the row.
+constexpr int kPerWave = 8;                     // so KS <= 32 (d_model <= 8192 at 256-wide slices)
 template <bool kE4M3>
-__global__ void __launch_bounds__(64) kv_proj_finish(int32_t T, int32_t KS, const float* __restrict__ part,
-                                                     const int32_t* __restrict__ pos,
-                                                     const int64_t* __restrict__ slot, void* __restrict__ cache,
-                                                     float* __restrict__ kv_scale, double log2_base) {
-  const int t = blockIdx.x, lane = threadIdx.x;
+__global__ void __launch_bounds__(256) kv_proj_finish(int32_t T, int32_t KS, const float* __restrict__ part,
+                                                      const int32_t* __restrict__ pos,
+                                                      const int64_t* __restrict__ slot, void* __restrict__ cache,
+                                                      float* __restrict__ kv_scale, double log2_base) {
+  __shared__ f32x4 red[3][2][64];
+  __shared__ f32x2 redk[3][64];
+  const int t = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x4 x0[kPerWave], x1[kPerWave];
+  f32x2 y[kPerWave];
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int j = min(wave + 4 * i, KS - 1);
+    const float* pr = part + ((int64_t)j * T + t) * kRow;
+    x0[i] = *reinterpret_cast<const f32x4*>(pr + 8 * lane);
+    x1[i] = *reinterpret_cast<const f32x4*>(pr + 8 * lane + 4);
+    y[i] = lane < 32 ? *reinterpret_cast<const f32x2*>(pr + 512 + 2 * lane) : f32x2{0.f, 0.f};
+  }
   f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
   f32x2 kr = {0.f, 0.f};
-  for (int j = 0; j < KS; ++j) {
-    const float* pr = part + ((int64_t)j * T + t) * kRow;
-    c0 += *reinterpret_cast<const f32x4*>(pr + 8 * lane);
-    c1 += *reinterpret_cast<const f32x4*>(pr + 8 * lane + 4);
-    if (lane < 32) kr += *reinterpret_cast<const f32x2*>(pr + 512 + 2 * lane);
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i)
+    if (wave + 4 * i < KS) {
+      c0 += x0[i];
+      c1 += x1[i];
+      kr += y[i];
+    }
+  if (wave > 0) {
+    red[wave - 1][0][lane] = c0;
+    red[wave - 1][1][lane] = c1;
+    redk[wave - 1][lane] = kr;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w) {
+    c0 += red[w][0][lane];
+    c1 += red[w][1][lane];
+    kr += redk[w][lane];
   }
   const u32x4_t c = {pack2_bf16(c0[0], c0[1]), pack2_bf16(c0[2], c0[3]), pack2_bf16(c1[0], c1[1]),
                      pack2_bf16(c1[2], c1[3])};
@@ -106,11 +147,10 @@ struct ProjPlan {
 
 ProjPlan plan_proj(const mla_dims& d, int32_t T, int32_t dm) {
   ProjPlan p{};
-  p.mfma = d.act_dtype == MLA_BF16 && d.d_latent == 512 && d.d_rope == 64 && dm % 32 == 0 &&
-           (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_E4M3);
-  const int32_t slices = std::max(1, std::min(dm / 32, (kTargetWaves + kFeatBlocks - 1) / kFeatBlocks));
-  p.kc = std::max(32, ((dm + slices - 1) / slices + 31) / 32 * 32);
+  p.kc = 32 * kSliceSteps;
   p.ks = (dm + p.kc - 1) / p.kc;
+  p.mfma = d.act_dtype == MLA_BF16 && d.d_latent == 512 && d.d_rope == 64 && dm % 32 == 0 &&
+           p.ks <= 4 * kPerWave && (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_E4M3);
   p.mfma_bytes = p.mfma ? (size_t)p.ks * T * kRow * sizeof(float) : 0;
   const size_t es = d.act_dtype == MLA_F32 ? 4 : 2;
   const size_t cb = ((size_t)T * d.d_latent * es + 255) & ~(size_t)255;
@@ -133,15 +173,15 @@ hipError_t launch_kv_project_append(const mla_dims& d, int32_t T, int32_t dm, co
                         reinterpret_cast<uintptr_t>(w_kr) | reinterpret_cast<uintptr_t>(cache)) % 16 == 0;
   if (p.mfma && aligned) {
     float* part = static_cast<float*>(ws);
-    kv_proj_partial<<<dim3(kFeatBlocks, p.ks), 64, 0, s>>>(T, dm, p.kc, static_cast<const uint16_t*>(h),
-                                                           static_cast<const uint16_t*>(w_dkv),
-                                                           static_cast<const uint16_t*>(w_kr), part);
+    kv_proj_partial<kSliceSteps><<<dim3(kFeatBlocks, p.ks), 64, 0, s>>>(T, dm, static_cast<const uint16_t*>(h),
+                                                                        static_cast<const uint16_t*>(w_dkv),
+                                                                        static_cast<const uint16_t*>(w_kr), part);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (d.kv_dtype == MLA_BF16)
-      kv_proj_finish<false><<<T, 64, 0, s>>>(T, p.ks, part, pos, slot, cache, kv_scale, std::log2(d.rope_base));
+      kv_proj_finish<false><<<T, 256, 0, s>>>(T, p.ks, part, pos, slot, cache, kv_scale, std::log2(d.rope_base));
     else
-      kv_proj_finish<true><<<T, 64, 0, s>>>(T, p.ks, part, pos, slot, cache, kv_scale, std::log2(d.rope_base));
+      kv_proj_finish<true><<<T, 256, 0, s>>>(T, p.ks, part, pos, slot, cache, kv_scale, std::log2(d.rope_base));
     return hipGetLastError();
   }
   const size_t es = d.act_dtype == MLA_F32 ? 4 : 2;
