@@ -181,6 +181,31 @@ def window_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, start: int, scale: float, 
                            q_pos=L - 1, k_pos=np.arange(start, L), k_r_rotated=k_r_rotated, heads=heads)
 
 
+def multi_query_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, scale: float, base: float, start: int = 0,
+                       k_r_rotated: bool = False, heads=None):
+    """Several new tokens of one sequence, each attending causally.
+
+    ([P4] "先区分 KV Cache 与 MLA": new tokens are appended, then attend over
+    history plus current; [P2] "第一步，训练时": a token attends over the
+    tokens up to itself.)  q_c [q, n_h, d_h], q_r [q, n_h, d_R]; the last q of
+    the L rows are the queries' own, so query i sits at position
+    p = L - q + i and attends to rows start .. p.  Returns per-query lists
+    stacked: out [q, heads, d_h], o_lat [q, heads, d_c], lse [q, heads]; a
+    query with no row (p < start) gets zeros and -inf.
+    """
+    q_c, q_r, c_kv, k_r = _f64(q_c), _f64(q_r), _f64(c_kv), _f64(k_r)
+    q, L = q_c.shape[0], c_kv.shape[0]
+    res = []
+    for i in range(q):
+        p = L - q + i
+        lo = min(max(int(start), 0), max(p + 1, 0))
+        hi = max(p + 1, 0)
+        res.append(explicit_decode(q_c[i], q_r[i], c_kv[lo:hi], k_r[lo:hi], w_uk, w_uv, scale=scale, base=base,
+                                   q_pos=p, k_pos=np.arange(lo, hi), k_r_rotated=k_r_rotated, heads=heads))
+    return dict(out=np.stack([r["out"] for r in res]), o_lat=np.stack([r["o_lat"] for r in res]),
+                lse=np.stack([r["lse"] for r in res]), heads=res[0]["heads"])
+
+
 # ----------------------------------------------------------------------------
 # Absorbed form ([P2] "第二步，推理时的吸收"; [P3] "3. 一个聪明的优化")
 # ----------------------------------------------------------------------------

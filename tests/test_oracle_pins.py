@@ -174,6 +174,52 @@ def test_window_ignores_rows_before_it_and_empty_window():
 
 
 # ---------------------------------------------------------------------------
+# Several new tokens per sequence, each attending causally (algomooc.com
+# "先区分 KV Cache 与 MLA"; keybo.xyz "第一步，训练时")
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("q,start", [(1, 0), (3, 0), (3, 2), (4, 5)])
+def test_multi_query_matches_brute_force(q, start):
+    rng = np.random.default_rng(300 + q + start)
+    n_h, d_h, d_c, d_r, L = 2, 3, 4, 4, 7
+    q_c, q_r = rng.standard_normal((q, n_h, d_h)), rng.standard_normal((q, n_h, d_r))
+    c_kv, k_r = rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r))
+    w_uk, w_uv = rng.standard_normal((n_h, d_h, d_c)), rng.standard_normal((n_h, d_h, d_c))
+    scale, base = 0.4, 50.0
+    res = O.multi_query_decode(q_c, q_r, c_kv, k_r, w_uk, w_uv, scale=scale, base=base, start=start)
+    for i in range(q):
+        p = L - q + i
+        if p < start:
+            assert np.all(res["o_lat"][i] == 0) and np.all(np.isneginf(res["lse"][i]))
+            continue
+        bo, bl, bs = _bf_decode(q_c[i].tolist(), q_r[i].tolist(), c_kv[:p + 1].tolist(), k_r[:p + 1].tolist(),
+                                w_uk.tolist(), w_uv.tolist(), scale, base, start=start)
+        np.testing.assert_allclose(res["out"][i], bo, rtol=0, atol=1e-13 * np.abs(bo).max())
+        np.testing.assert_allclose(res["o_lat"][i], bl, rtol=0, atol=1e-13 * np.abs(bl).max())
+        np.testing.assert_allclose(res["lse"][i], bs, rtol=0, atol=1e-13 * max(1, np.abs(bs).max()))
+
+
+def test_multi_query_is_causal():
+    """Changing the rows after a query's own position leaves it unchanged;
+    the last query sees everything."""
+    rng = np.random.default_rng(17)
+    n_h, d_h, d_c, d_r, L, q = 2, 4, 6, 4, 12, 4
+    args = [rng.standard_normal((q, n_h, d_h)), rng.standard_normal((q, n_h, d_r)),
+            rng.standard_normal((L, d_c)), rng.standard_normal((L, d_r)),
+            rng.standard_normal((n_h, d_h, d_c)), rng.standard_normal((n_h, d_h, d_c))]
+    kw = dict(scale=0.3, base=100.0)
+    a = O.multi_query_decode(*args, **kw)
+    args[2] = args[2].copy(); args[3] = args[3].copy()
+    args[2][L - 1] += 5.0
+    args[3][L - 1] -= 3.0
+    b = O.multi_query_decode(*args, **kw)
+    for k in ("out", "o_lat", "lse"):
+        np.testing.assert_array_equal(a[k][:q - 1], b[k][:q - 1])
+        assert not np.allclose(a[k][q - 1], b[k][q - 1])
+    full = O.explicit_decode(args[0][q - 1], args[1][q - 1], args[2], args[3], args[4], args[5], **kw)
+    np.testing.assert_allclose(b["out"][q - 1], full["out"], rtol=0, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
 # Rows straight from hidden states (keybo.xyz "第一步，训练时" and "RoPE 为什么必须解耦")
 # ---------------------------------------------------------------------------
 def test_projected_rows_of_unit_hidden_states_are_weight_columns():
