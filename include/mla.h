@@ -229,6 +229,43 @@ mla_status mla_decode_window(const mla_dims* dims, int32_t batch, const void* q_
                              void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream);
 
 /*
+ * mla_decode_multi_workspace_bytes - device workspace mla_decode_multi needs.
+ * Pure host computation; returns 0 when the arguments are invalid.
+ */
+size_t mla_decode_multi_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t num_splits);
+
+/*
+ * mla_decode_multi - several new query tokens per sequence (a chunk of new
+ * tokens, as in chunked prefill or when checking drafted tokens), each
+ * attending causally.
+ *   Source: algomooc.com MLA interview page, section "先区分 KV Cache 与 MLA"
+ *   (new tokens are appended, then attend over history plus current) and
+ *   keybo.xyz page, section "第一步，训练时" (every token attends over the
+ *   tokens up to itself); the absorbed score and latent sum as in mla_decode.
+ *
+ *   The last q_len rows of sequence b (positions L - q_len .. L - 1, L =
+ *   seq_lens[b], already appended) are its queries; query i attends to the
+ *   rows j with seq_starts[b] <= j <= L - q_len + i:
+ *     o_lat[b, i] and lse[b, i] = mla_decode_window of that query over those rows.
+ *   If L < q_len, the queries with no row of their own (i < q_len - L) get
+ *   o_lat = 0, lse = -inf.
+ *
+ *   q_abs  [batch, q_len, n_h, D]     act_dtype (mla_absorb_q with
+ *                                     batch * q_len rows, positions L - q_len + i)
+ *   o_lat  [batch, q_len, n_h, d_c]   act_dtype, written
+ *   lse    [batch, q_len, n_h]        float32, written (may be NULL)
+ *   seq_starts may be NULL (every start 0); other arguments as
+ *   mla_decode_window.  1 <= q_len; batch * q_len <= 2^24.  The rows of a
+ *   sequence's pages are read once per query token.
+ *   Errors: MLA_ERR_NULL, MLA_ERR_SHAPE, MLA_ERR_DTYPE, MLA_ERR_WORKSPACE.
+ */
+mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_abs,
+                            const void* kv_cache, const float* kv_scale, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts,
+                            int32_t num_splits, void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
+                            void* stream);
+
+/*
  * mla_up_v - the single W_UV up-projection after the latent weighted sum.
  *   Source: keybo.xyz page, section "第二步，推理时的吸收" (output identity).
  *

@@ -26,6 +26,9 @@ SIGNATURES = {
                              c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
     "mla_decode_window": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
+    "mla_decode_multi_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32, c_int32]),
+    "mla_decode_multi": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
+                                   c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
     "mla_up_v": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p]),
     "mla_status_string": (ctypes.c_char_p, [c_int32]),
     "mla_last_hip_error": (c_int32, []),

@@ -272,9 +272,9 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
 __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2,
     const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
-    const int32_t* __restrict__ block_table, int32_t max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
+    const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
   Lane ln;
   const int tid = threadIdx.x;
   ln.lane = tid & 63;
@@ -332,7 +332,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     const int64_t np = window_pages(seq_len(b), st, kBs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
-    const int32_t* bt = block_table + (int64_t)b * max_pages + fp;
+    const int32_t* bt = block_table + (int64_t)(b / bt_div) * max_pages + fp;   // bt_div sequences per row
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
@@ -564,7 +564,7 @@ bool mfma_decode_supported(const mla_dims& d) {
 
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
-                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* block_table, int32_t max_pages, int32_t bt_div,
                               const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
                               float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
   (void)kv_scale;
@@ -573,7 +573,7 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
   const int grid = ((W + 7) / 8) * 8 * HG;                  // 8 XCDs x ceil(W/8) parts x HG
   const float s2 = d.softmax_scale * 1.4426950408889634f;
   decode_mfma_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
-                                       static_cast<const uint16_t*>(cache), block_table, max_pages,
+                                       static_cast<const uint16_t*>(cache), block_table, max_pages, bt_div,
                                        seq_lens, seq_starts, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

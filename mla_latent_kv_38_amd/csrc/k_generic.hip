@@ -147,9 +147,9 @@ template <typename TQ, int KV>
 __global__ void __launch_bounds__(256) decode_generic(
     int32_t B, int32_t n_h, int32_t d_c, int32_t d_R, int32_t bs, int32_t W, float scale,
     const TQ* __restrict__ q_abs, const void* __restrict__ cache, const float* __restrict__ kv_scale,
-    const int32_t* __restrict__ block_table, int32_t max_pages, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o, float* __restrict__ ws_lse,
-    TQ* __restrict__ o_lat, float* __restrict__ lse) {
+    const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
+    const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
+    float* __restrict__ ws_lse, TQ* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ int32_t scan[257];
   __shared__ float tile[kGenRows * kGenMaxD];
   __shared__ float q[kGenMaxD];
@@ -182,7 +182,7 @@ __global__ void __launch_bounds__(256) decode_generic(
 #pragma unroll
     for (int k = 0; k < kCols; ++k) acc[k] = 0.f;
     for (int64_t jp = jp0; jp < jp1; ++jp) {
-      const int64_t page = block_table[(int64_t)b * max_pages + fp + jp];
+      const int64_t page = block_table[(int64_t)(b / bt_div) * max_pages + fp + jp];
       const int ntok = (int)min<int64_t>(bs, (int64_t)L - jp * bs);
       const int tlo = jp == 0 ? lo : 0;                          // rows before the window: masked, zeroed
       for (int t0 = tlo & ~(kGenRows - 1); t0 < ntok; t0 += kGenRows) {
@@ -440,21 +440,21 @@ hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, 
 template <typename TQ>
 static void decode_generic_dispatch(const mla_dims& d, const DecodePlan& plan, int32_t B,
                                     const void* q_abs, const void* cache, const float* kv_scale,
-                                    const int32_t* bt, int32_t max_pages, const int32_t* seq_lens,
-                                    const int32_t* seq_starts, float* ws_o, float* ws_lse, void* o_lat,
-                                    float* lse, hipStream_t s) {
+                                    const int32_t* bt, int32_t max_pages, int32_t bt_div,
+                                    const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
+                                    float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
   dim3 grid(plan.parts, d.n_heads);
   const TQ* q = static_cast<const TQ*>(q_abs);
   TQ* o = static_cast<TQ*>(o_lat);
   if (d.kv_dtype == MLA_F32)
     decode_generic<TQ, MLA_F32><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
   else if (d.kv_dtype == MLA_BF16)
     decode_generic<TQ, MLA_BF16><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
   else
     decode_generic<TQ, MLA_E4M3><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
   combine_kernel<TQ><<<dim3(B, d.n_heads), 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts,
       seq_lens, seq_starts, ws_o, ws_lse, o, lse);
 }
@@ -486,8 +486,8 @@ DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
 
 hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                          const void* cache, const float* kv_scale, const int32_t* block_table,
-                         int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts, void* ws,
-                         void* o_lat, float* lse, hipStream_t s) {
+                         int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
+                         const int32_t* seq_starts, void* ws, void* o_lat, float* lse, hipStream_t s) {
   float *ws_o, *ws_lse;
   workspace_split(d, plan, B, ws, &ws_o, &ws_lse);
   // the MFMA kernel loads 16-byte fragments and stores 8-byte groups
@@ -495,18 +495,52 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
                        (reinterpret_cast<uintptr_t>(cache) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(o_lat) % 8 == 0);
   if (plan.kernel == kDecodeBf16 && aligned)
-    return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
+    return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
                               seq_starts, ws_o, ws_lse, o_lat, lse, s);
   if (plan.kernel == kDecodeFp8 && aligned && reinterpret_cast<uintptr_t>(kv_scale) % 16 == 0)
-    return launch_decode_fp8(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
+    return launch_decode_fp8(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
                              seq_starts, ws_o, ws_lse, o_lat, lse, s);
   if (d.act_dtype == MLA_F32)
-    decode_generic_dispatch<float>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
-                                   seq_starts, ws_o, ws_lse, o_lat, lse, s);
+    decode_generic_dispatch<float>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div,
+                                   seq_lens, seq_starts, ws_o, ws_lse, o_lat, lse, s);
   else
-    decode_generic_dispatch<bf16_t>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, seq_lens,
-                                    seq_starts, ws_o, ws_lse, o_lat, lse, s);
+    decode_generic_dispatch<bf16_t>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div,
+                                    seq_lens, seq_starts, ws_o, ws_lse, o_lat, lse, s);
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Several query tokens per sequence (a chunk of new tokens): query i of
+// sequence b sits at position L_b - q + i and attends to the rows up to its
+// own, i.e. it is the decode of a sequence of length L_b - q + 1 + i over
+// the same pages.  Each (b, i) becomes such a sequence, b * q + i, with
+// block-table row b; these lengths and starts are written to the workspace.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) expand_queries(int32_t B, int32_t q, const int32_t* __restrict__ seq_lens,
+                                                      const int32_t* __restrict__ seq_starts,
+                                                      int32_t* __restrict__ v_lens, int32_t* __restrict__ v_starts) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (int64_t)B * q) return;
+  const int32_t b = static_cast<int32_t>(i / q), j = static_cast<int32_t>(i - (int64_t)b * q);
+  v_lens[i] = max(0, seq_lens[b] - q + 1 + j);
+  v_starts[i] = seq_starts ? seq_starts[b] : 0;
+}
+
+size_t multi_extra_bytes(int32_t B, int32_t q) { return (2 * (size_t)B * q * sizeof(int32_t) + 255) & ~(size_t)255; }
+
+hipError_t launch_decode_multi(const mla_dims& d, const DecodePlan& plan, int32_t B, int32_t q, const void* q_abs,
+                               const void* cache, const float* kv_scale, const int32_t* block_table,
+                               int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts, void* ws,
+                               void* o_lat, float* lse, hipStream_t s) {
+  int32_t* v_lens = static_cast<int32_t*>(ws);
+  int32_t* v_starts = v_lens + (size_t)B * q;
+  const int64_t n = (int64_t)B * q;
+  expand_queries<<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(B, q, seq_lens, seq_starts, v_lens,
+                                                                         v_starts);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_decode(d, plan, B * q, q_abs, cache, kv_scale, block_table, max_pages, q, v_lens, v_starts,
+                       static_cast<char*>(ws) + multi_extra_bytes(B, q), o_lat, lse, s);
 }
 
 hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,

@@ -11,6 +11,7 @@ thread_local int32_t g_last_hip_error = 0;
 
 constexpr int32_t kMaxWidth = 1024;   // d_head, d_latent + d_rope limit of the generic kernels
 constexpr int32_t kMaxModel = 1 << 20; // d_model limit of the fused projection
+constexpr int64_t kMaxRows = 1 << 24;  // batch x query tokens of one decode call
 
 bool valid_dtype(int32_t t, bool allow_e4m3) {
   return t == MLA_F32 || t == MLA_BF16 || (allow_e4m3 && t == MLA_E4M3);
@@ -88,8 +89,36 @@ mla_status mla_decode_window(const mla_dims* dims, int32_t batch, const void* q_
   const mla::DecodePlan plan = mla::plan_decode(*dims, batch, num_splits);
   if (workspace_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
   return hip_status(mla::launch_decode(*dims, plan, batch, q_abs, kv_cache, kv_scale, block_table,
-                                       max_pages, seq_lens, seq_starts, workspace, o_lat, lse,
+                                       max_pages, 1, seq_lens, seq_starts, workspace, o_lat, lse,
                                        static_cast<hipStream_t>(stream)));
+}
+
+size_t mla_decode_multi_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t num_splits) {
+  if (check_dims(dims) != MLA_OK || batch < 1 || q_len < 1 || (int64_t)batch * q_len > kMaxRows ||
+      num_splits < 0 || num_splits > 65536)
+    return 0;
+  return mla::multi_extra_bytes(batch, q_len) + mla::plan_decode(*dims, batch * q_len, num_splits).ws_bytes;
+}
+
+mla_status mla_decode_multi(const mla_dims* dims, int32_t batch, int32_t q_len, const void* q_abs,
+                            const void* kv_cache, const float* kv_scale, const int32_t* block_table,
+                            int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts,
+                            int32_t num_splits, void* workspace, size_t workspace_bytes, void* o_lat, float* lse,
+                            void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 1 || q_len < 1 || (int64_t)batch * q_len > kMaxRows || max_pages < 1 || num_splits < 0 ||
+      num_splits > 65536)
+    return MLA_ERR_SHAPE;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !workspace || !o_lat) return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return MLA_ERR_WORKSPACE;
+  const int32_t rows = batch * q_len;
+  const mla::DecodePlan plan = mla::plan_decode(*dims, rows, num_splits);
+  if (workspace_bytes < mla::multi_extra_bytes(batch, q_len) + plan.ws_bytes) return MLA_ERR_WORKSPACE;
+  return hip_status(mla::launch_decode_multi(*dims, plan, batch, q_len, q_abs, kv_cache, kv_scale, block_table,
+                                             max_pages, seq_lens, seq_starts, workspace, o_lat, lse,
+                                             static_cast<hipStream_t>(stream)));
 }
 
 mla_status mla_up_v(const mla_dims* dims, int32_t batch, const void* o_lat, const void* w_uv,

@@ -26,10 +26,18 @@ hipError_t launch_cache_append(const mla_dims& d, int32_t T, const void* c_kv, c
                                float* kv_scale, hipStream_t s);
 hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                          const void* cache, const float* kv_scale, const int32_t* block_table,
-                         int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts, void* ws,
-                         void* o_lat, float* lse, hipStream_t s);
+                         int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
+                         const int32_t* seq_starts, void* ws, void* o_lat, float* lse, hipStream_t s);
 hipError_t launch_up_v(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                        hipStream_t s);
+
+// q query tokens per sequence: B * q virtual sequences (see k_generic.hip);
+// the workspace holds multi_extra_bytes of lengths, then the decode's own.
+size_t multi_extra_bytes(int32_t B, int32_t q);
+hipError_t launch_decode_multi(const mla_dims& d, const DecodePlan& plan, int32_t B, int32_t q, const void* q_abs,
+                               const void* cache, const float* kv_scale, const int32_t* block_table,
+                               int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts, void* ws,
+                               void* o_lat, float* lse, hipStream_t s);
 
 size_t kv_project_workspace_bytes(const mla_dims& d, int32_t T, int32_t dm);
 hipError_t launch_kv_project_append(const mla_dims& d, int32_t T, int32_t dm, const void* h, const void* w_dkv,
@@ -54,11 +62,12 @@ bool mfma_decode_supported(const mla_dims& d);
 bool fp8_decode_supported(const mla_dims& d);
 hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                              const void* cache, const float* kv_scale, const int32_t* block_table,
-                             int32_t max_pages, const int32_t* seq_lens, const int32_t* seq_starts,
-                             float* ws_o, float* ws_lse, void* o_lat, float* lse, hipStream_t s);
+                             int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
+                             const int32_t* seq_starts, float* ws_o, float* ws_lse, void* o_lat, float* lse,
+                             hipStream_t s);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
-                              const int32_t* block_table, int32_t max_pages,
+                              const int32_t* block_table, int32_t max_pages, int32_t bt_div,
                               const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
                               float* ws_lse, void* o_lat, float* lse, hipStream_t s);
 

@@ -165,6 +165,40 @@ def decode(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_s
     return o_lat, lse
 
 
+def decode_multi(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_splits: int = 0,
+                 seq_starts=None, workspace=None, o_lat=None, lse=None, stream=None):
+    """q_len query tokens per sequence (q_abs [batch, q_len, n_h, D]), each
+    attending causally over its sequence's rows; returns (o_lat, lse) of
+    shapes [batch, q_len, n_h, d_c] and [batch, q_len, n_h]."""
+    at = _TORCH[d.act_dtype]
+    B, q = q_abs.shape[0], q_abs.shape[1]
+    D = d.d_latent + d.d_rope
+    _need(q_abs, "q_abs", at, (B, q, d.n_heads, D))
+    _need(kv_cache, "kv_cache", _kv_torch(d))
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be [batch, max_pages]")
+    _need(seq_lens, "seq_lens", torch.int32, (B,))
+    if seq_starts is not None:
+        _need(seq_starts, "seq_starts", torch.int32, (B,))
+    if d.kv_dtype == MLA_E4M3:
+        _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    need = int(_lib.lib().mla_decode_multi_workspace_bytes(ctypes.byref(d), B, q, num_splits))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
+    if o_lat is None:
+        o_lat = torch.empty((B, q, d.n_heads, d.d_latent), dtype=at, device=q_abs.device)
+    _need(o_lat, "o_lat", at, (B, q, d.n_heads, d.d_latent))
+    if lse is None:
+        lse = torch.empty((B, q, d.n_heads), dtype=torch.float32, device=q_abs.device)
+    _need(lse, "lse", torch.float32, (B, q, d.n_heads))
+    check(_lib.lib().mla_decode_multi(ctypes.byref(d), B, q, _ptr(q_abs), _ptr(kv_cache), _ptr(kv_scale),
+                                      _ptr(block_table), block_table.shape[1], _ptr(seq_lens), _ptr(seq_starts),
+                                      num_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                      _ptr(o_lat), _ptr(lse), _stream(stream)), "mla_decode_multi")
+    return o_lat, lse
+
+
 def up_v(d: Dims, o_lat, w_uv, out=None, stream=None):
     """out = W_UV o_lat per batch row and head."""
     at = _TORCH[d.act_dtype]
