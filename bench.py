@@ -216,6 +216,7 @@ def main():
         dec_us = call_us["decode"]
 
     kvp = kv_project_measure(mla, d, w, dev, B, args.min_replica_mb)
+    mq = multi_query_measure(mla, d, w, dev, reps, bt, lens, act, iters=20)
 
     # algorithmic work of one decode call
     toks = int(w.lens.sum())
@@ -259,6 +260,7 @@ def main():
         "roofline": roof,
         "cache_fill_GBps": round(cache_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
         "kv_project": kvp,
+        "multi_query": mq,
     }
 
     if not args.no_cpu:
@@ -318,6 +320,43 @@ def kv_project_measure(mla, d, w, dev, T, min_mb, d_model=5120, iters=50):
     return {"tokens": T, "d_model": d_model, "us": round(us, 3), "algorithmic_bytes": nbytes,
             "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "weight_copies": R,
             "launch": "graph"}
+
+
+def multi_query_measure(mla, d, w, dev, reps, bt, lens, act, q_len=4, iters=20):
+    """mla_decode_multi with q_len new query tokens per sequence (the last
+    q_len rows of each sequence are theirs) on the same caches: mean call time
+    and the HBM rate on the algorithmic bytes (every latent row once, the
+    queries, the outputs).  Each query token reads its rows separately, so
+    the rate is at most 1/q_len of the one-query decode's."""
+    import torch
+    B, nh, D = w.B, w.n_h, w.D
+    gen = torch.Generator(device=dev).manual_seed(11)
+    q_abs = torch.randn((B, q_len, nh, D), generator=gen, device=dev).to(act)
+    ws = torch.empty(int(mla._lib.lib().mla_decode_multi_workspace_bytes(__import__("ctypes").byref(d), B,
+                                                                          q_len, 0)),
+                     dtype=torch.uint8, device=dev)
+    o = torch.empty((B, q_len, nh, w.d_c), dtype=act, device=dev)
+    l = torch.empty((B, q_len, nh), dtype=torch.float32, device=dev)
+    R = len(reps)
+    for i in range(3):
+        rp = reps[i % R]
+        mla.decode_multi(d, q_abs, rp["cache"], bt, lens, kv_scale=rp["scale"], workspace=ws, o_lat=o, lse=l)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(iters):
+        rp = reps[i % R]
+        mla.decode_multi(d, q_abs, rp["cache"], bt, lens, kv_scale=rp["scale"], workspace=ws, o_lat=o, lse=l)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / iters * 1e3
+    esz = 1 if w.kv == "e4m3" else (2 if w.kv == "bf16" else 4)
+    asz = 2 if w.act == "bf16" else 4
+    nbytes = int(w.lens.sum()) * (D * esz + (4 if w.kv == "e4m3" else 0)) + B * q_len * nh * (D + w.d_c) * asz
+    gbps = nbytes / (us * 1e-6) / 1e9
+    return {"q_len": q_len, "us": round(us, 3), "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
+            "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
 def cpu_baseline(w, nseq, row_bytes):
