@@ -274,7 +274,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
     const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
+    float* __restrict__ ws_lse, int64_t* __restrict__ ws_tbl, uint16_t* __restrict__ o_lat,
+    float* __restrict__ lse) {
   Lane ln;
   const int tid = threadIdx.x;
   ln.lane = tid & 63;
@@ -333,6 +334,10 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
     const int32_t* bt = block_table + (int64_t)(b / bt_div) * max_pages + fp;   // bt_div sequences per row
+    if (jp0 == 0 && hg == 0 && threadIdx.x < 4) {                // the merge's part range of sequence b
+      const int64_t v[4] = {part, part_of_page(first + np - 1, pr.P, W), np, pr.P};
+      ws_tbl[4 * (int64_t)b + threadIdx.x] = v[threadIdx.x];
+    }
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
@@ -536,8 +541,8 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
   }
 }
 
-// One workgroup per (sequence, head group, wave-column block); the page
-// prefix gives the sequence's part range.  (Placing each workgroup on the XCD
+// One workgroup per (sequence, head group, wave-column block); the
+// sequence's part range comes from the decode kernel (ws_tbl).  (Placing each workgroup on the XCD
 // whose L2 the partials were written through measured no faster than this
 // plain order once the search it needed was counted.)
 __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32_t W, int32_t HG,
@@ -545,14 +550,18 @@ __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32
                                                    const int32_t* __restrict__ seq_starts,
                                                    const float* __restrict__ ws_o,
                                                    const float* __restrict__ ws_lse,
+                                                   const int64_t* __restrict__ ws_tbl,
                                                    uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
   const int per_seq = HG * 16;
   const int32_t b = blockIdx.x / per_seq;
   const int r = blockIdx.x % per_seq;
-  const SeqPages sp = seq_pages(seq_lens, seq_starts, B, kBs, b);
-  const int64_t w0 = sp.np > 0 ? part_of_page(sp.first, sp.P, W) : 0;
-  const int64_t w1 = sp.np > 0 ? part_of_page(sp.first + sp.np - 1, sp.P, W) : 0;
-  combine_item(b, r / 16, r % 16, n_h, W, sp.P, sp.np, w0, w1, ws_o, ws_lse, o_lat, lse);
+  // A sequence with pages has its part range in ws_tbl (written by the decode
+  // workgroup that took its first page); an empty one is known from its length.
+  const int64_t np = window_pages(seq_lens[b], seq_start(seq_starts, b), kBs);
+  const int64_t w0 = np > 0 ? ws_tbl[4 * (int64_t)b] : 0;
+  const int64_t w1 = np > 0 ? ws_tbl[4 * (int64_t)b + 1] : 0;
+  const int64_t P = np > 0 ? ws_tbl[4 * (int64_t)b + 3] : 0;
+  combine_item(b, r / 16, r % 16, n_h, W, P, np, w0, w1, ws_o, ws_lse, o_lat, lse);
 }
 
 }  // namespace
@@ -566,7 +575,7 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages, int32_t bt_div,
                               const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
-                              float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
+                              float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s) {
   (void)kv_scale;
   const int HG = d.n_heads / 64;
   const int W = plan.parts;
@@ -574,10 +583,11 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
   const float s2 = d.softmax_scale * 1.4426950408889634f;
   decode_mfma_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
                                        static_cast<const uint16_t*>(cache), block_table, max_pages, bt_div,
-                                       seq_lens, seq_starts, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
+                                       seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, static_cast<uint16_t*>(o_lat),
+                                       lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, seq_starts, ws_o, ws_lse,
+  combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl,
                                           static_cast<uint16_t*>(o_lat), lse);
   return hipGetLastError();
 }

@@ -460,12 +460,15 @@ static void decode_generic_dispatch(const mla_dims& d, const DecodePlan& plan, i
 }
 
 static void workspace_split(const mla_dims& d, const DecodePlan& plan, int32_t B, void* ws,
-                            float** ws_o, float** ws_lse) {
+                            float** ws_o, float** ws_lse, int64_t** ws_tbl) {
   const size_t slots = (size_t)plan.parts + B;
   size_t o_bytes = slots * d.n_heads * d.d_latent * sizeof(float);
   o_bytes = (o_bytes + 255) & ~(size_t)255;
+  size_t l_bytes = slots * d.n_heads * sizeof(float);
+  l_bytes = (l_bytes + 255) & ~(size_t)255;
   *ws_o = static_cast<float*>(ws);
   *ws_lse = reinterpret_cast<float*>(static_cast<char*>(ws) + o_bytes);
+  *ws_tbl = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + o_bytes + l_bytes);
 }
 
 DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
@@ -480,7 +483,7 @@ DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
   o_bytes = (o_bytes + 255) & ~(size_t)255;
   size_t l_bytes = slots * d.n_heads * sizeof(float);
   l_bytes = (l_bytes + 255) & ~(size_t)255;
-  p.ws_bytes = o_bytes + l_bytes;
+  p.ws_bytes = o_bytes + l_bytes + (size_t)batch * 4 * sizeof(int64_t);   // + per-sequence part range
   return p;
 }
 
@@ -489,14 +492,15 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
                          int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
                          const int32_t* seq_starts, void* ws, void* o_lat, float* lse, hipStream_t s) {
   float *ws_o, *ws_lse;
-  workspace_split(d, plan, B, ws, &ws_o, &ws_lse);
+  int64_t* ws_tbl;
+  workspace_split(d, plan, B, ws, &ws_o, &ws_lse, &ws_tbl);
   // the MFMA kernel loads 16-byte fragments and stores 8-byte groups
   const bool aligned = (reinterpret_cast<uintptr_t>(q_abs) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(cache) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(o_lat) % 8 == 0);
   if (plan.kernel == kDecodeBf16 && aligned)
     return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
-                              seq_starts, ws_o, ws_lse, o_lat, lse, s);
+                              seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   if (plan.kernel == kDecodeFp8 && aligned && reinterpret_cast<uintptr_t>(kv_scale) % 16 == 0)
     return launch_decode_fp8(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
                              seq_starts, ws_o, ws_lse, o_lat, lse, s);

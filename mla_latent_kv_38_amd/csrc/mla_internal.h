@@ -69,6 +69,6 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages, int32_t bt_div,
                               const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
-                              float* ws_lse, void* o_lat, float* lse, hipStream_t s);
+                              float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s);
 
 }  // namespace mla
