@@ -200,7 +200,8 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
     const uint16_t* __restrict__ q_abs, const uint8_t* __restrict__ cache, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
+    float* __restrict__ ws_lse, int64_t* __restrict__ ws_tbl, uint16_t* __restrict__ o_lat,
+    float* __restrict__ lse) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, s = lane & 15;
@@ -238,6 +239,10 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
     const int64_t jp1 = min(np, jp0 + (x1 - x));
     const int n = static_cast<int>(jp1 - jp0);                  // pages of this segment
     const int32_t* bt = block_table + (int64_t)(b / bt_div) * max_pages + fp;   // bt_div sequences per row
+    if (jp0 == 0 && hg == 0 && tid < 4) {                       // the merge's part range of sequence b
+      const int64_t v[4] = {part, part_of_page(first + np - 1, pr.P, W), np, pr.P};
+      ws_tbl[4 * (int64_t)b + tid] = v[tid];
+    }
 
     // The segment's first three pages into slots 0-2, and this head group's
     // 16 query rows (18 KiB, contiguous in q_abs) into slot 3, which is free
@@ -350,18 +355,19 @@ bool fp8_decode_supported(const mla_dims& d) {
 hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                              const void* cache, const float* kv_scale, const int32_t* block_table,
                              int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
-                             const int32_t* seq_starts, float* ws_o, float* ws_lse, void* o_lat, float* lse,
-                             hipStream_t s) {
+                             const int32_t* seq_starts, float* ws_o, float* ws_lse, int64_t* ws_tbl, void* o_lat,
+                             float* lse, hipStream_t s) {
   const int HG = d.n_heads / kHeads;
   const int W = plan.parts;
   const int grid = ((W + 7) / 8) * 8 * HG;                      // 8 XCDs x ceil(W/8) parts x HG
   const float s2 = d.softmax_scale * 1.4426950408889634f;
   decode_fp8_h16<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
                                       static_cast<const uint8_t*>(cache), kv_scale, block_table, max_pages,
-                                      bt_div, seq_lens, seq_starts, ws_o, ws_lse, static_cast<uint16_t*>(o_lat), lse);
+                                      bt_div, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl,
+                                      static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return launch_combine(d, plan, B, seq_lens, seq_starts, ws_o, ws_lse, o_lat, lse, s);
+  return launch_combine(d, plan, B, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
 }
 
 }  // namespace mla

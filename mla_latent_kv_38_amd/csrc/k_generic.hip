@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(256) decode_generic(
     const TQ* __restrict__ q_abs, const void* __restrict__ cache, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
-    float* __restrict__ ws_lse, TQ* __restrict__ o_lat, float* __restrict__ lse) {
+    float* __restrict__ ws_lse, int64_t* __restrict__ ws_tbl, TQ* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ int32_t scan[257];
   __shared__ float tile[kGenRows * kGenMaxD];
   __shared__ float q[kGenMaxD];
@@ -175,6 +175,10 @@ __global__ void __launch_bounds__(256) decode_generic(
     const int64_t np = window_pages(seq_lens[b], st, bs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
+    if (jp0 == 0 && h == 0 && tid < 4) {                         // the merge's part range of sequence b
+      const int64_t v[4] = {w, part_of_page(first + np - 1, P, W), np, P};
+      ws_tbl[4 * (int64_t)b + tid] = v[tid];
+    }
     __syncthreads();
     for (int i = tid; i < D; i += blockDim.x) q[i] = io<TQ>::load(q_abs, ((int64_t)b * n_h + h) * D + i);
     float m = -INFINITY, l = 0.f;
@@ -264,21 +268,12 @@ __global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int
                                                      const int32_t* __restrict__ seq_starts,
                                                      const float* __restrict__ ws_o,
                                                      const float* __restrict__ ws_lse,
+                                                     const int64_t* __restrict__ ws_tbl,
                                                      TO* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ float wgt[kCombMaxSeg];
   __shared__ int32_t slot[kCombMaxSeg];
   const int b = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  int64_t pre = 0, tot = 0;
-  for (int i = lane; i < B; i += 64) {
-    const int64_t np = window_pages(seq_lens[i], seq_start(seq_starts, i), bs);
-    tot += np;
-    if (i < b) pre += np;
-  }
-  for (int off = 32; off > 0; off >>= 1) {
-    pre += __shfl_xor(pre, off);
-    tot += __shfl_xor(tot, off);
-  }
-  const int64_t P = tot;
+  // part range of a sequence with pages: written by the decode kernel (ws_tbl)
   const int64_t np = window_pages(seq_lens[b], seq_start(seq_starts, b), bs);
   const int64_t row = (int64_t)b * n_h + h;
   if (np == 0) {
@@ -286,7 +281,7 @@ __global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int
     if (lane == 0 && lse) lse[row] = -INFINITY;
     return;
   }
-  const int64_t w0 = part_of_page(pre, P, W), w1 = part_of_page(pre + np - 1, P, W);
+  const int64_t w0 = ws_tbl[4 * (int64_t)b], w1 = ws_tbl[4 * (int64_t)b + 1], P = ws_tbl[4 * (int64_t)b + 3];
   if (w0 == w1) return;
   // reference max over the non-empty parts (parts inside [w0, w1] can be empty
   // when there are more parts than pages)
@@ -425,15 +420,15 @@ hipError_t launch_cache_append(const mla_dims& d, int32_t T_, const void* c_kv, 
 }
 
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
-                          const int32_t* seq_starts, const float* ws_o, const float* ws_lse, void* o_lat,
-                          float* lse, hipStream_t s) {
+                          const int32_t* seq_starts, const float* ws_o, const float* ws_lse, const int64_t* ws_tbl,
+                          void* o_lat, float* lse, hipStream_t s) {
   dim3 grid(B, d.n_heads);
   if (d.act_dtype == MLA_F32)
     combine_kernel<float><<<grid, 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts, seq_lens,
-                                               seq_starts, ws_o, ws_lse, static_cast<float*>(o_lat), lse);
+                                               seq_starts, ws_o, ws_lse, ws_tbl, static_cast<float*>(o_lat), lse);
   else
     combine_kernel<bf16_t><<<grid, 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts, seq_lens,
-                                                seq_starts, ws_o, ws_lse, static_cast<bf16_t*>(o_lat), lse);
+                                                seq_starts, ws_o, ws_lse, ws_tbl, static_cast<bf16_t*>(o_lat), lse);
   return hipGetLastError();
 }
 
@@ -442,21 +437,21 @@ static void decode_generic_dispatch(const mla_dims& d, const DecodePlan& plan, i
                                     const void* q_abs, const void* cache, const float* kv_scale,
                                     const int32_t* bt, int32_t max_pages, int32_t bt_div,
                                     const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
-                                    float* ws_lse, void* o_lat, float* lse, hipStream_t s) {
+                                    float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s) {
   dim3 grid(plan.parts, d.n_heads);
   const TQ* q = static_cast<const TQ*>(q_abs);
   TQ* o = static_cast<TQ*>(o_lat);
   if (d.kv_dtype == MLA_F32)
     decode_generic<TQ, MLA_F32><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o, lse);
   else if (d.kv_dtype == MLA_BF16)
     decode_generic<TQ, MLA_BF16><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o, lse);
   else
     decode_generic<TQ, MLA_E4M3><<<grid, 256, 0, s>>>(B, d.n_heads, d.d_latent, d.d_rope, d.block_size, plan.parts,
-        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+        d.softmax_scale, q, cache, kv_scale, bt, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o, lse);
   combine_kernel<TQ><<<dim3(B, d.n_heads), 64, 0, s>>>(B, d.n_heads, d.d_latent, d.block_size, plan.parts,
-      seq_lens, seq_starts, ws_o, ws_lse, o, lse);
+      seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o, lse);
 }
 
 static void workspace_split(const mla_dims& d, const DecodePlan& plan, int32_t B, void* ws,
@@ -503,13 +498,13 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
                               seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   if (plan.kernel == kDecodeFp8 && aligned && reinterpret_cast<uintptr_t>(kv_scale) % 16 == 0)
     return launch_decode_fp8(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
-                             seq_starts, ws_o, ws_lse, o_lat, lse, s);
+                             seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   if (d.act_dtype == MLA_F32)
     decode_generic_dispatch<float>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div,
-                                   seq_lens, seq_starts, ws_o, ws_lse, o_lat, lse, s);
+                                   seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   else
     decode_generic_dispatch<bf16_t>(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div,
-                                    seq_lens, seq_starts, ws_o, ws_lse, o_lat, lse, s);
+                                    seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   return hipGetLastError();
 }
 

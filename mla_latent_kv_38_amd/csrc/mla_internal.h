@@ -45,8 +45,8 @@ hipError_t launch_kv_project_append(const mla_dims& d, int32_t T, int32_t dm, co
                                     float* kv_scale, void* ws, hipStream_t s);
 
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
-                          const int32_t* seq_starts, const float* ws_o, const float* ws_lse, void* o_lat,
-                          float* lse, hipStream_t s);
+                          const int32_t* seq_starts, const float* ws_o, const float* ws_lse, const int64_t* ws_tbl,
+                          void* o_lat, float* lse, hipStream_t s);
 
 // MFMA projections (bf16); *handled = false when the shapes or alignments are
 // not covered, and the caller then runs the generic kernel.
@@ -63,8 +63,8 @@ bool fp8_decode_supported(const mla_dims& d);
 hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                              const void* cache, const float* kv_scale, const int32_t* block_table,
                              int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
-                             const int32_t* seq_starts, float* ws_o, float* ws_lse, void* o_lat, float* lse,
-                             hipStream_t s);
+                             const int32_t* seq_starts, float* ws_o, float* ws_lse, int64_t* ws_tbl, void* o_lat,
+                             float* lse, hipStream_t s);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages, int32_t bt_div,
