@@ -283,6 +283,61 @@ __global__ void __launch_bounds__(64) combine_kernel(int32_t B, int32_t n_h, int
   }
   const int64_t w0 = ws_tbl[4 * (int64_t)b], w1 = ws_tbl[4 * (int64_t)b + 1], P = ws_tbl[4 * (int64_t)b + 3];
   if (w0 == w1) return;
+  const int64_t nparts = w1 - w0 + 1;
+  if (nparts <= 64 && d_c % 4 == 0 && d_c <= 1024) {
+    // One lane per part: its lse (-inf for a part without pages) and weight,
+    // then the partial rows four parts at a time with all their loads in
+    // flight together (three dependent memory round trips in all).
+    float e = -INFINITY;
+    if (lane < nparts) {
+      const int64_t w = w0 + lane;
+      if (part_start(w, P, W) < part_start(w + 1, P, W)) e = ws_lse[(w + b) * n_h + h];
+    }
+    float M = e;
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    const float wl = e == -INFINITY ? 0.f : expf(e - M);
+    float denom = wl;
+    for (int off = 32; off > 0; off >>= 1) denom += __shfl_xor(denom, off);
+    const int ncol4 = d_c / 4;
+    float4 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < nparts; k0 += 4) {
+      float wk[4];
+      float4 v[4][4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int k = min<int64_t>(k0 + i, nparts - 1);
+        wk[i] = k0 + i < nparts ? __shfl(wl, k) : 0.f;
+        const float4* src = reinterpret_cast<const float4*>(ws_o + ((w0 + k + b) * n_h + h) * d_c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int c4 = lane + 64 * j;
+          v[i][j] = (wk[i] != 0.f && c4 < ncol4) ? src[c4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[j].x += wk[i] * v[i][j].x; acc[j].y += wk[i] * v[i][j].y;
+          acc[j].z += wk[i] * v[i][j].z; acc[j].w += wk[i] * v[i][j].w;
+        }
+    }
+    const float inv = 1.f / denom;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int c4 = lane + 64 * j;
+      if (c4 < ncol4) {
+        io<TO>::store(o_lat, row * d_c + 4 * c4 + 0, acc[j].x * inv);
+        io<TO>::store(o_lat, row * d_c + 4 * c4 + 1, acc[j].y * inv);
+        io<TO>::store(o_lat, row * d_c + 4 * c4 + 2, acc[j].z * inv);
+        io<TO>::store(o_lat, row * d_c + 4 * c4 + 3, acc[j].w * inv);
+      }
+    }
+    if (lane == 0 && lse) lse[row] = M + logf(denom);
+    return;
+  }
   // reference max over the non-empty parts (parts inside [w0, w1] can be empty
   // when there are more parts than pages)
   float M = -INFINITY;

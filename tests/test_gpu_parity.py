@@ -128,3 +128,13 @@ def test_fp8_chain(lens, splits):
     w = W.make("fp8_h16_b128", B=len(lens), lens=lens)
     res = C.run_chain(w, num_splits=splits)
     _check_all(w, res)
+
+
+@pytest.mark.parametrize("splits", [40, 150])
+def test_generic_merge_few_and_many_parts(splits):
+    """The generic kernel's merge (16 heads, bf16 cache) with a sequence
+    spread over fewer than 64 parts (one part per lane) and over more (the
+    general loop, with empty parts inside the range)."""
+    w = W.make("v2_b16_4k", B=2, lens=[4096, 700], n_h=16, shuffle=True)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res)
