@@ -39,6 +39,8 @@ def parse():
     p.add_argument("--min-replica-mb", type=float, default=600.0)
     p.add_argument("--cpu-sample-seqs", type=int, default=2)
     p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="skip the fused-projection and multi-query measurements (profiling runs)")
     p.add_argument("--graph", action="store_true",
                    help="replay each step from a captured HIP graph (one graph per cache replica)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -215,8 +217,10 @@ def main():
     if dec_us is None:                   # graph replay: the decode call is timed in the eager pass
         dec_us = call_us["decode"]
 
-    kvp = kv_project_measure(mla, d, w, dev, B, args.min_replica_mb)
-    mq = multi_query_measure(mla, d, w, dev, reps, bt, lens, act, iters=20)
+    kvp = mq = None
+    if not args.no_extras:
+        kvp = kv_project_measure(mla, d, w, dev, B, args.min_replica_mb)
+        mq = multi_query_measure(mla, d, w, dev, reps, bt, lens, act, iters=20)
 
     # algorithmic work of one decode call
     toks = int(w.lens.sum())
