@@ -162,9 +162,11 @@ def main():
         rp = reps[i % R]
         rec = (lambda k: ev[k].record(stream) if ev[k] is not None else None) if ev is not None else (lambda k: None)
         rec(0)
-        mla.absorb_q(d, q_c, q_r, q_pos, rp["w_uk"], q_abs)
+        # absorb_q and the current token's append are independent: one call
+        # (one launch for these shapes); mla_absorb_q + mla_cache_append
+        # compute the same bytes
+        mla.absorb_q_append(d, q_c, q_r, q_pos, rp["w_uk"], *cur, rp["cache"], rp["scale"], q_abs=q_abs)
         rec(1)
-        mla.cache_append(d, *cur, rp["cache"], rp["scale"])
         rec(2)
         mla.decode(d, q_abs, rp["cache"], bt, lens, kv_scale=rp["scale"], num_splits=args.splits,
                    workspace=ws, o_lat=o_lat, lse=lse)
@@ -213,7 +215,7 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
     call_us = {name: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
-               for k, name in enumerate(["absorb_q", "cache_append", "decode", "up_v"])}
+               for k, name in ((0, "absorb_q_append"), (2, "decode"), (3, "up_v"))}
     if dec_us is None:                   # graph replay: the decode call is timed in the eager pass
         dec_us = call_us["decode"]
 

@@ -124,6 +124,22 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t n_tokens, const void* 
                             int64_t num_pages, void* kv_cache, float* kv_scale, void* stream);
 
 /*
+ * mla_absorb_q_append - mla_absorb_q and mla_cache_append in one call (they
+ * are independent: the query of step t and the row of token t), so that a
+ * decode step pays one kernel launch for both where the shapes allow.
+ *   Sources: as mla_absorb_q and mla_cache_append.
+ *
+ *   Exactly mla_absorb_q(dims, batch, q_c, q_r, q_pos, w_uk, q_abs) and
+ *   mla_cache_append(dims, n_tokens, c_kv, k_r, pos, slot, num_pages,
+ *   kv_cache, kv_scale): the same results bit for bit.  n_tokens = 0 appends
+ *   nothing.  Arguments, layouts and errors: as the two calls.
+ */
+mla_status mla_absorb_q_append(const mla_dims* dims, int32_t batch, const void* q_c, const void* q_r,
+                               const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t n_tokens,
+                               const void* c_kv, const void* k_r, const int32_t* pos, const int64_t* slot,
+                               int64_t num_pages, void* kv_cache, float* kv_scale, void* stream);
+
+/*
  * mla_kv_project_workspace_bytes - device workspace mla_kv_project_append
  * needs for n_tokens tokens of width d_model.  Pure host computation;
  * returns 0 when the arguments are invalid.

@@ -474,6 +474,19 @@ hipError_t launch_cache_append(const mla_dims& d, int32_t T_, const void* c_kv, 
   return hipGetLastError();
 }
 
+hipError_t launch_absorb_q_append(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
+                                  const int32_t* q_pos, const void* w_uk, void* q_abs, const AppendArgs& app,
+                                  hipStream_t s) {
+  bool handled = false;
+  if (app.T > 0) {
+    hipError_t e = launch_absorb_q_mfma(d, B, q_c, q_r, q_pos, w_uk, q_abs, s, &handled, &app);
+    if (handled || e != hipSuccess) return e;
+  }
+  hipError_t e = launch_absorb_q(d, B, q_c, q_r, q_pos, w_uk, q_abs, s);   // separately when not covered
+  if (e != hipSuccess || app.T == 0) return e;
+  return launch_cache_append(d, app.T, app.c_kv, app.k_r, app.pos, app.slot, app.cache, app.kv_scale, s);
+}
+
 hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, const int32_t* seq_lens,
                           const int32_t* seq_starts, const float* ws_o, const float* ws_lse, const int64_t* ws_tbl,
                           void* o_lat, float* lse, hipStream_t s) {

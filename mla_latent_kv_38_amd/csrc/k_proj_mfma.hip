@@ -48,16 +48,41 @@ constexpr int kAbsRowB = kAbsCols * 2 + 16;     // padded LDS row (bytes)
 // fragments are loaded together with the weight tile.
 constexpr int kMaxBlk = 4;
 
+// An independent append of new 576-wide rows can ride along in the same
+// launch (mla_absorb_q_append): the workgroups past the absorb grid (row y = 0)
+// each write four rows, one per wave, with the append's own row writer.
+struct AppendJob {
+  int32_t T;                       // rows to append (0: none)
+  int32_t e4m3;                    // cache type: E4M3 (1) or bf16 (0)
+  const uint16_t* c_kv;
+  const uint16_t* k_r;
+  const int32_t* pos;
+  const int64_t* slot;
+  void* cache;
+  float* kv_scale;
+};
+
 template <int kKs>   // d_h / 32
 __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t bpw, int32_t n_h, int32_t d_c, int32_t d_R,
                                                      const uint16_t* __restrict__ q_c,
                                                      const uint16_t* __restrict__ q_r,
                                                      const int32_t* __restrict__ pos,
                                                      const uint16_t* __restrict__ w_uk,
-                                                     uint16_t* __restrict__ q_abs, double log2_base) {
+                                                     uint16_t* __restrict__ q_abs, double log2_base,
+                                                     AppendJob app) {
   constexpr int d_h = 32 * kKs;
   __shared__ __attribute__((aligned(16))) char tile[d_h * kAbsRowB];
   const int cblocks = d_c / kAbsCols;
+  if (blockIdx.x >= n_h * cblocks) {                             // the ride-along append
+    const int t = 4 * (blockIdx.x - n_h * cblocks) + (threadIdx.x >> 6), ln = threadIdx.x & 63;
+    if (blockIdx.y != 0 || t >= app.T) return;
+    const u32x4_t c = *reinterpret_cast<const u32x4_t*>(app.c_kv + (int64_t)t * 512 + 8 * ln);
+    uint32_t kp = 0;
+    if (ln < 32) kp = *reinterpret_cast<const uint32_t*>(app.k_r + (int64_t)t * 64 + 2 * ln);
+    if (app.e4m3) append_row_576<true>(c, kp, app.pos[t], app.slot[t], app.cache, app.kv_scale, log2_base, ln);
+    else append_row_576<false>(c, kp, app.pos[t], app.slot[t], app.cache, app.kv_scale, log2_base, ln);
+    return;
+  }
   const int h = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
   const int c0 = cb * kAbsCols;
   const int b_lo = blockIdx.y * bpw, b_hi = min(B, b_lo + bpw);
@@ -245,8 +270,17 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
                                 const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t s,
-                                bool* handled) {
+                                bool* handled, const AppendArgs* append) {
   *handled = false;
+  AppendJob app{};
+  if (append) {                    // only the 576-wide bf16-input append rides along
+    if (!(d.d_latent == 512 && d.d_rope == 64 && (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_E4M3) &&
+          aligned16(append->c_kv) && aligned16(append->cache) && (reinterpret_cast<uintptr_t>(append->k_r) & 3u) == 0))
+      return hipSuccess;
+    app = AppendJob{append->T, d.kv_dtype == MLA_E4M3, static_cast<const uint16_t*>(append->c_kv),
+                    static_cast<const uint16_t*>(append->k_r), append->pos, append->slot, append->cache,
+                    append->kv_scale};
+  }
   const int D = d.d_latent + d.d_rope;
   if (d.act_dtype != MLA_BF16 || d.d_latent % kAbsCols != 0 || d.d_head % 32 != 0 || D % 4 != 0 ||
       !aligned16(q_c) || !aligned16(w_uk) || !aligned16(q_abs) || (reinterpret_cast<uintptr_t>(q_r) & 3u))
@@ -258,16 +292,16 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, c
   int nsplit = std::max((nblocks + kMaxBlk - 1) / kMaxBlk, std::min(nblocks, (256 + wgs - 1) / wgs));
   const int bpw = 16 * ((nblocks + nsplit - 1) / nsplit);
   nsplit = (B + bpw - 1) / bpw;
-  const dim3 grid(wgs, nsplit);
+  const dim3 grid(wgs + (app.T + 3) / 4, nsplit);
   auto qc = static_cast<const uint16_t*>(q_c);
   auto qr = static_cast<const uint16_t*>(q_r);
   auto w = static_cast<const uint16_t*>(w_uk);
   auto qa = static_cast<uint16_t*>(q_abs);
   switch (d.d_head) {
-    case 64:  absorb_q_mfma<2><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
-    case 128: absorb_q_mfma<4><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
-    case 192: absorb_q_mfma<6><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
-    case 256: absorb_q_mfma<8><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base)); break;
+    case 64:  absorb_q_mfma<2><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base), app); break;
+    case 128: absorb_q_mfma<4><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base), app); break;
+    case 192: absorb_q_mfma<6><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base), app); break;
+    case 256: absorb_q_mfma<8><<<grid, 256, 0, s>>>(B, bpw, d.n_heads, d.d_latent, d.d_rope, qc, qr, pos, w, qa, std::log2(d.rope_base), app); break;
     default: return hipSuccess;
   }
   *handled = true;

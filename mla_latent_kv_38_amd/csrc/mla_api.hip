@@ -63,6 +63,23 @@ mla_status mla_cache_append(const mla_dims* dims, int32_t n_tokens, const void* 
                                              kv_scale, static_cast<hipStream_t>(stream)));
 }
 
+mla_status mla_absorb_q_append(const mla_dims* dims, int32_t batch, const void* q_c, const void* q_r,
+                               const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t n_tokens,
+                               const void* c_kv, const void* k_r, const int32_t* pos, const int64_t* slot,
+                               int64_t num_pages, void* kv_cache, float* kv_scale, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 1 || n_tokens < 0 || num_pages < 1) return MLA_ERR_SHAPE;
+  if (!q_c || !q_pos || !w_uk || !q_abs || (dims->d_rope > 0 && !q_r)) return MLA_ERR_NULL;
+  if (n_tokens > 0) {
+    if (!c_kv || !pos || !slot || !kv_cache || (dims->d_rope > 0 && !k_r)) return MLA_ERR_NULL;
+    if (dims->kv_dtype == MLA_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  }
+  const mla::AppendArgs app{n_tokens, c_kv, k_r, pos, slot, kv_cache, kv_scale};
+  return hip_status(mla::launch_absorb_q_append(*dims, batch, q_c, q_r, q_pos, w_uk, q_abs, app,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t num_splits) {
   if (check_dims(dims) != MLA_OK || batch < 1 || num_splits < 0 || num_splits > 65536) return 0;
   return mla::plan_decode(*dims, batch, num_splits).ws_bytes;

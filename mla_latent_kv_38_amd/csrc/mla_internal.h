@@ -8,6 +8,17 @@ namespace mla {
 // Number of compute units the launch geometry is planned for (MI355X).
 constexpr int kNumCU = 256;
 
+// An append carried by the absorb_q launch (mla_absorb_q_append).
+struct AppendArgs {
+  int32_t T;
+  const void* c_kv;
+  const void* k_r;
+  const int32_t* pos;
+  const int64_t* slot;
+  void* cache;
+  float* kv_scale;
+};
+
 enum DecodeKernel { kDecodeGeneric = 0, kDecodeBf16 = 1, kDecodeFp8 = 2 };
 
 struct DecodePlan {
@@ -24,6 +35,9 @@ hipError_t launch_absorb_q(const mla_dims& d, int32_t B, const void* q_c, const 
 hipError_t launch_cache_append(const mla_dims& d, int32_t T, const void* c_kv, const void* k_r,
                                const int32_t* pos, const int64_t* slot, void* cache,
                                float* kv_scale, hipStream_t s);
+hipError_t launch_absorb_q_append(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
+                                  const int32_t* q_pos, const void* w_uk, void* q_abs, const AppendArgs& app,
+                                  hipStream_t s);
 hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                          const void* cache, const float* kv_scale, const int32_t* block_table,
                          int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
@@ -48,11 +62,13 @@ hipError_t launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t B, 
                           const int32_t* seq_starts, const float* ws_o, const float* ws_lse, const int64_t* ws_tbl,
                           void* o_lat, float* lse, hipStream_t s);
 
+
 // MFMA projections (bf16); *handled = false when the shapes or alignments are
-// not covered, and the caller then runs the generic kernel.
+// not covered (for absorb_q, including those of the carried append, if any),
+// and the caller then runs the generic kernels.
 hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, const void* q_r,
                                 const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t s,
-                                bool* handled);
+                                bool* handled, const AppendArgs* append = nullptr);
 hipError_t launch_up_v_mfma(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                             hipStream_t s, bool* handled);
 

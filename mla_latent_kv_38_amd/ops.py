@@ -90,6 +90,39 @@ def cache_append(d: Dims, c_kv, k_r, pos, slot, kv_cache, kv_scale=None, stream=
           "mla_cache_append")
 
 
+def absorb_q_append(d: Dims, q_c, q_r, q_pos, w_uk, c_kv, k_r, pos, slot, kv_cache, kv_scale=None, q_abs=None,
+                    stream=None):
+    """absorb_q and cache_append in one call (one launch where the shapes
+    allow); returns q_abs."""
+    at = _TORCH[d.act_dtype]
+    B = q_c.shape[0]
+    D = d.d_latent + d.d_rope
+    _need(q_c, "q_c", at, (B, d.n_heads, d.d_head))
+    if d.d_rope:
+        _need(q_r, "q_r", at, (B, d.n_heads, d.d_rope))
+    _need(q_pos, "q_pos", torch.int32, (B,))
+    _need(w_uk, "w_uk", at, (d.n_heads, d.d_head, d.d_latent))
+    if q_abs is None:
+        q_abs = torch.empty((B, d.n_heads, D), dtype=at, device=q_c.device)
+    _need(q_abs, "q_abs", at, (B, d.n_heads, D))
+    T = c_kv.shape[0]
+    _need(c_kv, "c_kv", at, (T, d.d_latent))
+    if d.d_rope:
+        _need(k_r, "k_r", at, (T, d.d_rope))
+    _need(pos, "pos", torch.int32, (T,))
+    _need(slot, "slot", torch.int64, (T,))
+    _need(kv_cache, "kv_cache", _kv_torch(d))
+    if kv_cache.dim() != 3 or kv_cache.shape[1] != d.block_size or kv_cache.shape[2] != D:
+        raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)}")
+    if d.kv_dtype == MLA_E4M3:
+        _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    check(_lib.lib().mla_absorb_q_append(ctypes.byref(d), B, _ptr(q_c), _ptr(q_r), _ptr(q_pos), _ptr(w_uk),
+                                         _ptr(q_abs), T, _ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot),
+                                         kv_cache.shape[0], _ptr(kv_cache), _ptr(kv_scale), _stream(stream)),
+          "mla_absorb_q_append")
+    return q_abs
+
+
 def kv_project_workspace_bytes(d: Dims, n_tokens: int, d_model: int) -> int:
     return int(_lib.lib().mla_kv_project_workspace_bytes(ctypes.byref(d), n_tokens, d_model))
 

@@ -84,3 +84,43 @@ def test_vector_append_matches_oracle(kv):
         gs = r["scale"].view(-1)[torch.from_numpy(r["slots"]).cuda()].cpu().numpy()
         assert (got != codes).mean() <= 1e-5
         assert np.all(np.abs(gs - s) <= 2.0 ** -23 * np.abs(s))
+
+
+@pytest.mark.parametrize("kv", ["bf16", "e4m3"])
+@pytest.mark.parametrize("T,misalign", [(0, False), (16, False), (37, False), (16, True)])
+def test_absorb_q_append_equals_the_two_calls(kv, T, misalign):
+    """mla_absorb_q_append (one launch when the shapes allow; the two launches
+    otherwise, here forced by a misaligned latent buffer) leaves the same bytes
+    in q_abs and in the cache as mla_absorb_q followed by mla_cache_append."""
+    w = W.make("v2_b16_4k", B=16, lens=[1] * 16, seed=8)
+    rng = np.random.default_rng(T + 3)
+    d = mla.make_dims(w.n_h, w.d_h, w.d_c, w.d_R, w.block_size, act="bf16", kv=kv,
+                      softmax_scale=w.scale, rope_base=w.rope_base)
+    c = W.round_to(rng.standard_normal((max(T, 1), 512)), "bf16")[:T]
+    k = W.round_to(rng.standard_normal((max(T, 1), 64)), "bf16")[:T]
+    pos = rng.integers(0, 1 << 16, size=T).astype(np.int32)
+    pages = 3
+    slots = rng.permutation(pages * 64)[:T].astype(np.int64)
+    qpos = rng.integers(0, 1 << 16, size=16).astype(np.int32)
+    args_q = (_dev(w.q_c, torch.bfloat16), _dev(w.q_r, torch.bfloat16), _dev(qpos, torch.int32),
+              _dev(w.w_uk, torch.bfloat16))
+    args_a = (_dev(c, torch.bfloat16, misalign), _dev(k, torch.bfloat16), _dev(pos, torch.int32),
+              _dev(slots, torch.int64))
+
+    def cache():
+        if kv == "e4m3":
+            return (torch.zeros((pages, 64, 576), dtype=torch.uint8, device="cuda"),
+                    torch.zeros((pages, 64), dtype=torch.float32, device="cuda"))
+        return torch.zeros((pages, 64, 576), dtype=torch.bfloat16, device="cuda"), None
+
+    c1, s1 = cache()
+    q1 = mla.absorb_q(d, *args_q)
+    if T:
+        mla.cache_append(d, *args_a, c1, s1)
+    c2, s2 = cache()
+    q2 = mla.absorb_q_append(d, *args_q, *args_a, c2, s2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.view(torch.int16), q2.view(torch.int16))
+    assert torch.equal(c1.view(torch.uint8), c2.view(torch.uint8))
+    if kv == "e4m3":
+        assert torch.equal(s1, s2)
