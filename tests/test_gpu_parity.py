@@ -138,3 +138,21 @@ def test_generic_merge_few_and_many_parts(splits):
     w = W.make("v2_b16_4k", B=2, lens=[4096, 700], n_h=16, shuffle=True)
     res = C.run_chain(w, num_splits=splits)
     _check_all(w, res)
+
+
+@pytest.mark.parametrize("n_h,splits", [(64, 0), (64, 37), (16, 0)])
+def test_batch_larger_than_a_workgroup(n_h, splits):
+    """More sequences than threads in a workgroup (the part locators then sum
+    several sequences per thread), with empty and one-token sequences among
+    them; a sample of sequences is checked."""
+    rng = np.random.default_rng(77)
+    lens = rng.integers(0, 200, size=300)
+    lens[[5, 6, 150]] = 0
+    lens[[7, 299]] = 1
+    w = W.make("v2_b16_4k", B=300, lens=lens, n_h=n_h, shuffle=True)
+    res = C.run_chain(w, num_splits=splits)
+    seqs = [0, 5, 7, 8, 149, 150, 151, 298, 299]
+    for b in seqs:
+        if w.lens[b] == 0:
+            assert np.all(C.f64(res["o_lat"][b]) == 0) and np.all(np.isneginf(C.f64(res["lse"][b])))
+    _check_all(w, res, heads=[0, n_h - 1], seqs=[b for b in seqs if w.lens[b] > 0])
