@@ -39,6 +39,9 @@ WORKLOADS = {
                          lens=("const", 131072), act="bf16", kv="bf16", shuffle=False),
     "fp8_h16_b128": dict(kind="latent", B=128, n_h=16, d_h=128, d_c=512, d_R=64,
                          lens=("uniform", 512, 4096), act="bf16", kv="e4m3", shuffle=True),
+    # the headline shapes with an E4M3 cache (all 128 heads on one GPU)
+    "v2_b16_4k_e4m3": dict(kind="latent", B=16, n_h=128, d_h=128, d_c=512, d_R=64,
+                           lens=("const", 4096), act="bf16", kv="e4m3", shuffle=False),
 }
 
 BLOCK_SIZE = 64

@@ -43,6 +43,10 @@ constexpr int kRowB = 1168;                 // 1152 data bytes + 16 pad (73 x 16
 constexpr int kPageB = kBs * kRowB;         // 74752 = 73 x 1 KiB
 constexpr int kPtRowB = 144;                // P^T row: 64 bf16 + 16 pad
 constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
+constexpr int kCodesB = kBs * kD;           // 36864: one page of E4M3 codes (also its stride in the cache)
+constexpr int kCodePageB = kCodesB;
+constexpr int kCodeSlotB = kCodesB + kBs * 4;   // ring slot: codes, then the page's 64 float32 scales
+static_assert(2 * kCodeSlotB <= kPageB, "two code slots share the second page buffer");
 
 
 // Copy one 64-token page (64 x 1152 B) into the padded LDS tile: 73 direct
@@ -81,6 +85,41 @@ __device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&offa)
     w.ch += 37;
     w.row += 3;
     if (w.ch >= 73) { w.ch -= 73; w.row += 1; }
+  }
+}
+
+// Two E4M3 codes (the low or high half of a dword) -> two bfloat16: the
+// scaled conversion with scale 1.0 is exact for every code (each E4M3 value
+// is a bfloat16 value).
+template <bool kHi>
+__device__ __forceinline__ uint32_t cvt_pair(uint32_t codes) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, kHi));
+}
+
+// One page of E4M3 codes (64 rows x 576, unpadded) -> the padded bf16 tile.
+// Thread t converts the 8-code groups v = t + 256 k, k < 18 (row v / 72,
+// group v % 72): 8-byte reads and 16-byte writes, each linear across the
+// wave.  Rows outside [lo, nvalid) are written as zeros.
+__device__ __forceinline__ void convert_page(const LDSP char* __restrict__ codes, LDSP char* __restrict__ tile,
+                                             int nvalid, int lo) {
+  const int tid = threadIdx.x;
+  int row = tid / 72, g = tid - 72 * (tid / 72);
+  const bool full = nvalid == kBs && lo == 0;
+#pragma unroll
+  for (int k0 = 0; k0 < 18; k0 += 6) {
+    u32x2 c[6];
+#pragma unroll
+    for (int j = 0; j < 6; ++j) c[j] = *(const LDSP u32x2*)(codes + 8 * (tid + 256 * (k0 + j)));
+#pragma unroll
+    for (int j = 0; j < 6; ++j) {
+      u32x4 o = {cvt_pair<false>(c[j][0]), cvt_pair<true>(c[j][0]), cvt_pair<false>(c[j][1]),
+                 cvt_pair<true>(c[j][1])};
+      if (!full && (row < lo || row >= nvalid)) o = u32x4{0u, 0u, 0u, 0u};
+      *(LDSP u32x4*)(tile + row * kRowB + 16 * g) = o;
+      g += 40;                                     // 256 groups = 3 rows + 40 groups
+      row += 3;
+      if (g >= 72) { g -= 72; row += 1; }
+    }
   }
 }
 
@@ -138,20 +177,42 @@ struct Acc {                       // per-segment running state of one wave
 // buf (read) and nbuf (direct-load target) are __restrict__: the compiler
 // then knows the in-flight loads into nbuf never alias reads of buf and adds
 // no waits of its own (the explicit vmcnt + barrier at the top orders them).
+//
+// E4M3 cache (kE4M3): buf is the bf16 tile and stays put; the codes of this
+// page are in the ring slot `codes` (rows of 576 codes, then 64 float32
+// scales) and nbuf is the other slot, which receives the next page.  The
+// page is converted into the tile first (masked rows as zeros), and the
+// per-token scale s_t multiplies the scores and P (row = s_t * codes).
+template <bool kE4M3>
 __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict__ buf,
                                           LDSP char* __restrict__ nbuf,
                                           bool dma, const char* cbase, const int32_t* bt_after,
                                           int32_t& pg_after, const uint32_t (&offa)[19],
-                                          const bf16x8 (&qf)[36], int nvalid, int lo, float s2, Acc& acc) {
+                                          const bf16x8 (&qf)[36], int nvalid, int lo, float s2, Acc& acc,
+                                          const LDSP char* __restrict__ codes = nullptr,
+                                          const char* sbase = nullptr) {
   LDSP char* pt = (LDSP char*)g_pt;
   float* xm = g_xm;
   float* xa = g_xa;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();                                               // this page landed; previous one consumed
   asm volatile("" : "+v"(pg_after));                             // its load (one page ago) has landed
-  const char* nsrc_u = uniform(cbase + (int64_t)pg_after * (kBs * kD * 2));   // next page
+  const char* nsrc_u = uniform(cbase + (int64_t)pg_after * (kE4M3 ? kCodePageB : kBs * kD * 2));   // next page
   const uint32_t nbuf_u = uniform_lds(nbuf);
   const int32_t pg2 = bt_after ? *bt_after : 0;                  // page id two ahead, read during this page
+
+  if constexpr (kE4M3) {
+    if (dma) {                                                   // next page's codes and scales
+#pragma unroll
+      for (int i = 0; i < 9; ++i) {
+        const uint32_t k = static_cast<uint32_t>(ln.wave + 4 * i);
+        dma16_u(nsrc_u, 1024u * k + 16u * ln.lane, nbuf_u + 1024u * k);
+      }
+      if (ln.wave == 0) dma4(sbase + (int64_t)pg_after * (kBs * 4), 4 * ln.lane, nbuf + kCodesB);
+    }
+    convert_page(codes, buf, nvalid, lo);
+    barrier_lds();                                               // tile written
+  }
 
   // The two head groups of a part share an L2.  Waves of matching parity
   // (wave & 1 == head group) load their half of the next page during QK, the
@@ -159,8 +220,22 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   // early half has reached the L2: each 128-B line comes from HBM once and
   // each CU waits for HBM latency on only half of its page.
   const bool early = (ln.wave & 1) == ln.hg_part;
-  f32x16 S = dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
-                          : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
+  f32x16 S = !kE4M3 && dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
+                                    : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
+
+  // E4M3: score_t = s_t (q . codes_t); the scale of a masked row is taken
+  // as 0 so that whatever its slot holds cannot reach P.
+  float sct[16];
+  if constexpr (kE4M3) {
+    const LDSP float* sc = (const LDSP float*)(codes + kCodesB);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ra = r >> 2;
+      const int t = 32 * ln.th + 16 * (ra >> 1) + 2 * (ra & 1) + ln.hi + 4 * (r & 3);
+      sct[r] = (t >= nvalid || t < lo) ? 0.f : sc[t];
+      S[r] *= sct[r];
+    }
+  }
 
   // Scores stay raw (s2 > 0 commutes with the maximum); rows past the end of
   // the sequence, and rows before the start of its window, are -inf.  P below
@@ -194,7 +269,8 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], s2, -acc.m_ref));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], s2, -acc.m_ref));
       ps += p0 + p1;
-      pk[r >> 1] = pack2_bf16(p0, p1);
+      if constexpr (kE4M3) pk[r >> 1] = pack2_bf16(p0 * sct[r], p1 * sct[r + 1]);
+      else pk[r >> 1] = pack2_bf16(p0, p1);
     }
 #pragma unroll
     for (int ra = 0; ra < 4; ++ra) {
@@ -203,7 +279,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     }
   };
   make_p();
-  if (nvalid < kBs || lo > 0) {                                  // masked rows: zero the latent
+  if (!kE4M3 && (nvalid < kBs || lo > 0)) {                      // masked rows: zero the latent
     for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 64; i += 256) {
       const int k = i >> 6, ch = i & 63;
       const int row = k < lo ? k : nvalid + (k - lo);
@@ -257,11 +333,11 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n"
                  "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
                  : "+v"(acc.o[cb][0]), "+v"(acc.o[cb][1]) : "v"(vcur), "v"(pc0), "v"(pc1));
-    if (dma && !early) dma16_u(nsrc_u, offa[step], nbuf_u + 1024 * (ln.wave + 4 * step));
+    if (!kE4M3 && dma && !early) dma16_u(nsrc_u, offa[step], nbuf_u + 1024 * (ln.wave + 4 * step));
     vcur = vnext;
     if (cb == 3) { pc0 = pn0; pc1 = pn1; }
   }
-  if (dma && !early) {
+  if (!kE4M3 && dma && !early) {
     dma16_u(nsrc_u, offa[16], nbuf_u + 1024 * (ln.wave + 64));
     dma16_u(nsrc_u, offa[17], nbuf_u + 1024 * (ln.wave + 68));
     if (ln.wave == 0) dma16_u(nsrc_u, offa[18], nbuf_u + 1024 * 72);
@@ -269,9 +345,10 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   pg_after = pg2;
 }
 
+template <bool kE4M3>
 __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2,
-    const uint16_t* __restrict__ q_abs, const uint16_t* __restrict__ cache,
+    const uint16_t* __restrict__ q_abs, const void* __restrict__ cache, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, int64_t* __restrict__ ws_tbl, uint16_t* __restrict__ o_lat,
@@ -321,7 +398,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   dma_offsets(ln.wave, ln.lane, offa);
   const int ndma = dma_count(ln.wave);
   const char* cbase = reinterpret_cast<const char*>(cache);
-  constexpr int64_t kPageBytesG = (int64_t)kBs * kD * 2;
+  const char* sbase = reinterpret_cast<const char*>(kv_scale);
+  constexpr int64_t kPageBytesG = kE4M3 ? (int64_t)kCodePageB : (int64_t)kBs * kD * 2;
 
   for (;;) {
     // The window [st, L) of sequence b: its pages start at page fp; L and the
@@ -341,7 +419,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
-    // 1, both as whole 1 KiB direct loads.
+    // 1, both as whole 1 KiB direct loads.  E4M3: the queries go to the tile
+    // (buffer 0) and the first page's codes and scales to ring slot 0.
     int32_t pg0, pg_next;
     Acc acc;                                                     // cleared while the first loads are in flight
 #pragma unroll
@@ -354,7 +433,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     acc.l_own = 0.f;
     {                                                            // queries first: they need no page id
       const char* qsrc_u = uniform(reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD));
-      const uint32_t q_m0 = uniform_lds((LDSP char*)g_page1);
+      const uint32_t q_m0 = uniform_lds(kE4M3 ? (LDSP char*)g_page0 : (LDSP char*)g_page1);
 #pragma unroll
       for (int i = 0; i < 19; ++i)
         if (i < ndma) dma16_u(qsrc_u, offa[i], q_m0 + 1024 * (ln.wave + 4 * i));
@@ -362,21 +441,37 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       // when the segment has it)
       sload2_i32(bt + jp0, bt + (jp0 + 1 < jp1 ? jp0 + 1 : jp0), &pg0, &pg_next);
       const char* src_u = uniform(cbase + (int64_t)pg0 * kPageBytesG);
-      const uint32_t p_m0 = uniform_lds((LDSP char*)g_page0);
+      if constexpr (kE4M3) {
+        const uint32_t p_m0 = uniform_lds((LDSP char*)g_page1);
 #pragma unroll
-      for (int i = 0; i < 19; ++i)
-        if (i < ndma) dma16_u(src_u, offa[i], p_m0 + 1024 * (ln.wave + 4 * i));
+        for (int i = 0; i < 9; ++i) {
+          const uint32_t k = static_cast<uint32_t>(ln.wave + 4 * i);
+          dma16_u(src_u, 1024u * k + 16u * ln.lane, p_m0 + 1024u * k);
+        }
+        if (ln.wave == 0) dma4(sbase + (int64_t)pg0 * (kBs * 4), 4 * ln.lane, (LDSP char*)g_page1 + kCodesB);
+      } else {
+        const uint32_t p_m0 = uniform_lds((LDSP char*)g_page0);
+#pragma unroll
+        for (int i = 0; i < 19; ++i)
+          if (i < ndma) dma16_u(src_u, offa[i], p_m0 + 1024 * (ln.wave + 4 * i));
+      }
     }
     // Wait for this wave's query loads only (issued before the page's, and
     // direct loads complete in order): the first page keeps landing while
     // the queries are read into registers; its own wait is at the page top.
-    if (ndma == 19) asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
-    else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    if constexpr (kE4M3) {
+      if (ln.wave == 0) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+    } else {
+      if (ndma == 19) asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
+    }
     barrier_lds();
     // Q^T fragments stay in AGPRs for the whole segment (the MFMAs read them there)
     bf16x8 qf[36];
     {
-      const LDSP char* qrow = (LDSP char*)g_page1 + (ln.hb * 32 + ln.l32) * kRowB + ln.hi * 16;
+      const LDSP char* qrow = (kE4M3 ? (LDSP char*)g_page0 : (LDSP char*)g_page1) +
+                              (ln.hb * 32 + ln.l32) * kRowB + ln.hi * 16;
       bf16x8 t[36];
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) t[kb] = *(const LDSP bf16x8*)(qrow + 32 * kb);
@@ -397,8 +492,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
       const int nvalid = min(kBs, Lu - jp * kBs);                 // jp * 64 < L: no overflow
       const bool more = jp + 1 < j1;
-      page_step(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
-                nvalid, jp == 0 ? lo : 0, s2, acc);
+      if constexpr (kE4M3) {
+        LDSP char* cur = (LDSP char*)g_page1 + (even ? 0 : kCodeSlotB);
+        LDSP char* nxt = (LDSP char*)g_page1 + (even ? kCodeSlotB : 0);
+        page_step<true>(ln, (LDSP char*)g_page0, nxt, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next,
+                        offa, qf, nvalid, jp == 0 ? lo : 0, s2, acc, cur, sbase);
+      } else {
+        page_step<false>(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
+                         nvalid, jp == 0 ? lo : 0, s2, acc);
+      }
     }
 
     // ---- segment epilogue: normalise and store ------------------------------
@@ -567,8 +669,8 @@ __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32
 }  // namespace
 
 bool mfma_decode_supported(const mla_dims& d) {
-  return d.act_dtype == MLA_BF16 && d.kv_dtype == MLA_BF16 && d.d_latent == kDc && d.d_rope == 64 &&
-         d.block_size == kBs && d.n_heads % 64 == 0;
+  return d.act_dtype == MLA_BF16 && (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_E4M3) && d.d_latent == kDc &&
+         d.d_rope == 64 && d.block_size == kBs && d.n_heads % 64 == 0;
 }
 
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
@@ -576,15 +678,14 @@ hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t
                               const int32_t* block_table, int32_t max_pages, int32_t bt_div,
                               const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
                               float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s) {
-  (void)kv_scale;
   const int HG = d.n_heads / 64;
   const int W = plan.parts;
   const int grid = ((W + 7) / 8) * 8 * HG;                  // 8 XCDs x ceil(W/8) parts x HG
   const float s2 = d.softmax_scale * 1.4426950408889634f;
-  decode_mfma_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs),
-                                       static_cast<const uint16_t*>(cache), block_table, max_pages, bt_div,
-                                       seq_lens, seq_starts, ws_o, ws_lse, ws_tbl, static_cast<uint16_t*>(o_lat),
-                                       lse);
+  auto kern = d.kv_dtype == MLA_E4M3 ? decode_mfma_h64<true> : decode_mfma_h64<false>;
+  kern<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs), cache, kv_scale,
+                            block_table, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl,
+                            static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl,

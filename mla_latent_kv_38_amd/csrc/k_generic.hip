@@ -536,8 +536,8 @@ static void workspace_split(const mla_dims& d, const DecodePlan& plan, int32_t B
 
 DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
   DecodePlan p{};
-  p.kernel = mfma_decode_supported(d) ? kDecodeBf16 : fp8_decode_supported(d) ? kDecodeFp8 : kDecodeGeneric;
-  p.head_groups = p.kernel == kDecodeBf16 ? d.n_heads / 64 : p.kernel == kDecodeFp8 ? d.n_heads / 16 : d.n_heads;
+  p.kernel = mfma_decode_supported(d) ? kDecodeH64 : fp8_decode_supported(d) ? kDecodeFp8 : kDecodeGeneric;
+  p.head_groups = p.kernel == kDecodeH64 ? d.n_heads / 64 : p.kernel == kDecodeFp8 ? d.n_heads / 16 : d.n_heads;
   // one workgroup per CU for the MFMA kernels; the generic kernel runs 4 per CU
   int32_t autos = p.kernel != kDecodeGeneric ? (kNumCU / p.head_groups) : (kNumCU * 4) / d.n_heads;
   p.parts = num_splits > 0 ? num_splits : (autos > 0 ? autos : 1);
@@ -561,7 +561,8 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
   const bool aligned = (reinterpret_cast<uintptr_t>(q_abs) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(cache) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(o_lat) % 8 == 0);
-  if (plan.kernel == kDecodeBf16 && aligned)
+  if (plan.kernel == kDecodeH64 && aligned &&
+      (d.kv_dtype != MLA_E4M3 || reinterpret_cast<uintptr_t>(kv_scale) % 4 == 0))
     return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
                               seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   if (plan.kernel == kDecodeFp8 && aligned && reinterpret_cast<uintptr_t>(kv_scale) % 16 == 0)

@@ -19,7 +19,7 @@ struct AppendArgs {
   float* kv_scale;
 };
 
-enum DecodeKernel { kDecodeGeneric = 0, kDecodeBf16 = 1, kDecodeFp8 = 2 };
+enum DecodeKernel { kDecodeGeneric = 0, kDecodeH64 = 1, kDecodeFp8 = 2 };
 
 struct DecodePlan {
   int32_t parts;          // W: KV chunks the flattened page list is cut into

@@ -34,6 +34,7 @@ CASES = {
     "ragged_b64": dict(seqs=[0, 37, 63], heads=[1, 100]),
     "long_b4_128k": dict(seqs=[0, 3], heads=[0, 77]),
     "fp8_h16_b128": dict(seqs=[0, 64, 127], heads=[0, 9, 15]),
+    "v2_b16_4k_e4m3": dict(seqs=[0, 15], heads=[0, 64, 127]),
 }
 
 

@@ -103,6 +103,12 @@ def test_multi_fp8(q, splits):
     _check(w, res, qc, qr, q)
 
 
+def test_multi_fp8_64_heads():
+    w, qc, qr, qpos = _case("v2_b16_4k_e4m3", [513, 64, 700], 4, n_h=64, seed=27)
+    res = _run(w, qc, qr, qpos, 4, 7)
+    _check(w, res, qc, qr, 4)
+
+
 def test_multi_generic():
     w, qc, qr, qpos = _case("v2_b16_4k", [200, 65], 3, n_h=16, seed=31)
     res = _run(w, qc, qr, qpos, 3, 4)

@@ -130,6 +130,30 @@ def test_fp8_chain(lens, splits):
     _check_all(w, res)
 
 
+@pytest.mark.parametrize("n_h,lens,splits", [(128, [513, 64, 1000], 0), (64, [4096, 1, 700], 9),
+                                             (128, [130, 4000, 63, 700], 150)])
+def test_fp8_64_head_groups(n_h, lens, splits):
+    """The E4M3 cache at head counts that are multiples of 64: the 64-head
+    kernel (codes converted to bf16 in LDS, per-token scales on the scores and
+    on P), with ragged last pages, a one-row sequence and more parts than
+    pages."""
+    w = W.make("v2_b16_4k_e4m3", B=len(lens), lens=lens, n_h=n_h, shuffle=True)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res)
+
+
+def test_fp8_64_head_page_permutation_is_bitwise_invariant():
+    import copy
+    a = W.make("v2_b16_4k_e4m3", B=2, lens=[700, 300], n_h=64, shuffle=False)
+    b = copy.copy(a)
+    perm = np.random.default_rng(12).permutation(a.num_pages).astype(np.int32)
+    b.block_table = np.where(a.block_table >= 0, perm[np.maximum(a.block_table, 0)], -1).astype(np.int32)
+    assert not np.array_equal(a.block_table, b.block_table)
+    ra, rb = C.run_chain(a, num_splits=5), C.run_chain(b, num_splits=5)
+    for k in ("o_lat", "lse", "out"):
+        assert torch.equal(ra[k], rb[k]), k
+
+
 @pytest.mark.parametrize("splits", [40, 150])
 def test_generic_merge_few_and_many_parts(splits):
     """The generic kernel's merge (16 heads, bf16 cache) with a sequence

@@ -122,6 +122,13 @@ def test_window_fp8(splits):
     _check(w, res, starts)
 
 
+@pytest.mark.parametrize("splits", [0, 7])
+def test_window_fp8_64_heads(splits):
+    w = W.make("v2_b16_4k_e4m3", B=len(LENS), lens=LENS, n_h=64, shuffle=True)
+    res = _window_run(w, STARTS, splits)
+    _check(w, res, STARTS)
+
+
 def test_window_all_starts_zero_equals_plain_decode():
     w = W.make("ragged_b64", B=3, lens=[200, 450, 130])
     plain = C.run_chain(w, num_splits=4)
