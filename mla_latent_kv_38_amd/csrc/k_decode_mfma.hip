@@ -33,6 +33,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 #define LDSP __attribute__((address_space(3)))
 
@@ -43,10 +44,10 @@ constexpr int kRowB = 1168;                 // 1152 data bytes + 16 pad (73 x 16
 constexpr int kPageB = kBs * kRowB;         // 74752 = 73 x 1 KiB
 constexpr int kPtRowB = 144;                // P^T row: 64 bf16 + 16 pad
 constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
-constexpr int kCodesB = kBs * kD;           // 36864: one page of E4M3 codes (also its stride in the cache)
-constexpr int kCodePageB = kCodesB;
-constexpr int kCodeSlotB = kCodesB + kBs * 4;   // ring slot: codes, then the page's 64 float32 scales
-static_assert(2 * kCodeSlotB <= kPageB, "two code slots share the second page buffer");
+constexpr int kCodePageB = kBs * kD;        // 36864: one page of E4M3 codes in the cache
+constexpr int kRowC = 592;                  // E4M3 row in LDS: 576 codes + 16 pad (37 x 16 B)
+constexpr int kCodeRowsB = kBs * kRowC;     // 37888; the page's 64 float32 scales follow
+static_assert(kCodeRowsB + kBs * 4 <= kPageB, "an E4M3 page fits a page buffer");
 
 
 // Copy one 64-token page (64 x 1152 B) into the padded LDS tile: 73 direct
@@ -96,31 +97,50 @@ __device__ __forceinline__ uint32_t cvt_pair(uint32_t codes) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, kHi));
 }
 
-// One page of E4M3 codes (64 rows x 576, unpadded) -> the padded bf16 tile.
-// Thread t converts the 8-code groups v = t + 256 k, k < 18 (row v / 72,
-// group v % 72): 8-byte reads and 16-byte writes, each linear across the
-// wave.  Rows outside [lo, nvalid) are written as zeros.
-__device__ __forceinline__ void convert_page(const LDSP char* __restrict__ codes, LDSP char* __restrict__ tile,
-                                             int nvalid, int lo) {
-  const int tid = threadIdx.x;
-  int row = tid / 72, g = tid - 72 * (tid / 72);
-  const bool full = nvalid == kBs && lo == 0;
+__device__ __forceinline__ bf16x8 cvt8(u32x2 c) {      // 8 codes -> 8 bfloat16, in order
+  return __builtin_bit_cast(bf16x8, u32x4{cvt_pair<false>(c[0]), cvt_pair<true>(c[0]), cvt_pair<false>(c[1]),
+                                          cvt_pair<true>(c[1])});
+}
+
+// Copy one E4M3 page (64 x 576 codes, then 64 float32 scales) into a page
+// buffer with rows padded to 37 x 16 B: LDS slot q = 64 k + lane holds row
+// q / 37, 16-B chunk q % 37 (chunk 36 is padding and re-reads chunk 0);
+// 37 direct loads, wave w issuing k = w, w + 4, ...; wave 0 also loads the
+// scales.  Per wave: 10 loads (wave 0: 11 with the scales) or 9.
+__device__ __forceinline__ void dma_code_page(const char* src_u, uint32_t dst_u, const char* ssrc,
+                                              LDSP char* sdst, int wave, int lane) {
+  const int q0 = 64 * wave + lane;
+  int row = q0 / 37, ch = q0 - 37 * (q0 / 37);
 #pragma unroll
-  for (int k0 = 0; k0 < 18; k0 += 6) {
-    u32x2 c[6];
-#pragma unroll
-    for (int j = 0; j < 6; ++j) c[j] = *(const LDSP u32x2*)(codes + 8 * (tid + 256 * (k0 + j)));
-#pragma unroll
-    for (int j = 0; j < 6; ++j) {
-      u32x4 o = {cvt_pair<false>(c[j][0]), cvt_pair<true>(c[j][0]), cvt_pair<false>(c[j][1]),
-                 cvt_pair<true>(c[j][1])};
-      if (!full && (row < lo || row >= nvalid)) o = u32x4{0u, 0u, 0u, 0u};
-      *(LDSP u32x4*)(tile + row * kRowB + 16 * g) = o;
-      g += 40;                                     // 256 groups = 3 rows + 40 groups
-      row += 3;
-      if (g >= 72) { g -= 72; row += 1; }
-    }
+  for (int i = 0; i < 10; ++i) {
+    if (wave + 4 * i < 37)
+      dma16_u(src_u, static_cast<uint32_t>(row * kD + (ch == 36 ? 0 : 16 * ch)), dst_u + 1024u * (wave + 4 * i));
+    row += 6;                                        // 256 slots = 6 rows + 34 chunks
+    ch += 34;
+    if (ch >= 37) { ch -= 37; row += 1; }
   }
+  if (wave == 0) dma4(ssrc, 4 * lane, sdst);
+}
+
+// S^T for one wave from an E4M3 page: as qk_page, with each 8-code A
+// fragment converted in registers just before its MFMA.
+__device__ __forceinline__ f32x16 qk_page_e4m3(const LDSP char* __restrict__ ap, const bf16x8 (&qf)[36]) {
+  f32x16 S;
+  constexpr int kPre = 4;
+  u32x2 cf[kPre];
+#pragma unroll
+  for (int kb = 0; kb < kPre; ++kb) cf[kb] = *(const LDSP u32x2*)(ap + 16 * kb);
+#pragma unroll
+  for (int kb = 0; kb < 36; ++kb) {
+    const bf16x8 a = cvt8(cf[kb % kPre]);
+    if (kb + kPre < 36) cf[kb % kPre] = *(const LDSP u32x2*)(ap + 16 * (kb + kPre));
+    if (kb == 0)
+      asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(S) : "v"(a), "a"(qf[0]));
+    else
+      asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "a"(qf[kb]));
+  }
+  asm volatile("s_nop 7\n s_nop 7\n s_nop 3" ::: "memory");       // MFMA result -> VALU
+  return S;
 }
 
 // S^T[32 tokens x 32 heads] = C[32 x 576] . Q^T for one wave: 36 MFMAs fed
@@ -178,10 +198,8 @@ struct Acc {                       // per-segment running state of one wave
 // then knows the in-flight loads into nbuf never alias reads of buf and adds
 // no waits of its own (the explicit vmcnt + barrier at the top orders them).
 //
-// E4M3 cache (kE4M3): buf is the bf16 tile and stays put; the codes of this
-// page are in the ring slot `codes` (rows of 576 codes, then 64 float32
-// scales) and nbuf is the other slot, which receives the next page.  The
-// page is converted into the tile first (masked rows as zeros), and the
+// E4M3 cache (kE4M3): the buffers hold code rows of 592 B and the page's
+// scales; both contractions convert their fragments in registers, and the
 // per-token scale s_t multiplies the scores and P (row = s_t * codes).
 template <bool kE4M3>
 __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict__ buf,
@@ -189,7 +207,6 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
                                           bool dma, const char* cbase, const int32_t* bt_after,
                                           int32_t& pg_after, const uint32_t (&offa)[19],
                                           const bf16x8 (&qf)[36], int nvalid, int lo, float s2, Acc& acc,
-                                          const LDSP char* __restrict__ codes = nullptr,
                                           const char* sbase = nullptr) {
   LDSP char* pt = (LDSP char*)g_pt;
   float* xm = g_xm;
@@ -201,18 +218,8 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   const uint32_t nbuf_u = uniform_lds(nbuf);
   const int32_t pg2 = bt_after ? *bt_after : 0;                  // page id two ahead, read during this page
 
-  if constexpr (kE4M3) {
-    if (dma) {                                                   // next page's codes and scales
-#pragma unroll
-      for (int i = 0; i < 9; ++i) {
-        const uint32_t k = static_cast<uint32_t>(ln.wave + 4 * i);
-        dma16_u(nsrc_u, 1024u * k + 16u * ln.lane, nbuf_u + 1024u * k);
-      }
-      if (ln.wave == 0) dma4(sbase + (int64_t)pg_after * (kBs * 4), 4 * ln.lane, nbuf + kCodesB);
-    }
-    convert_page(codes, buf, nvalid, lo);
-    barrier_lds();                                               // tile written
-  }
+  if (kE4M3 && dma)                                               // next page's codes and scales, now
+    dma_code_page(nsrc_u, nbuf_u, sbase + (int64_t)pg_after * (kBs * 4), nbuf + kCodeRowsB, ln.wave, ln.lane);
 
   // The two head groups of a part share an L2.  Waves of matching parity
   // (wave & 1 == head group) load their half of the next page during QK, the
@@ -220,14 +227,16 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   // early half has reached the L2: each 128-B line comes from HBM once and
   // each CU waits for HBM latency on only half of its page.
   const bool early = (ln.wave & 1) == ln.hg_part;
-  f32x16 S = !kE4M3 && dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
-                                    : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
+  f32x16 S;
+  if constexpr (kE4M3) S = qk_page_e4m3(buf + ln.a_off, qf);
+  else S = dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
+                        : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
 
   // E4M3: score_t = s_t (q . codes_t); the scale of a masked row is taken
   // as 0 so that whatever its slot holds cannot reach P.
   float sct[16];
   if constexpr (kE4M3) {
-    const LDSP float* sc = (const LDSP float*)(codes + kCodesB);
+    const LDSP float* sc = (const LDSP float*)(buf + kCodeRowsB);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int ra = r >> 2;
@@ -279,11 +288,19 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     }
   };
   make_p();
-  if (!kE4M3 && (nvalid < kBs || lo > 0)) {                      // masked rows: zero the latent
-    for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 64; i += 256) {
-      const int k = i >> 6, ch = i & 63;
-      const int row = k < lo ? k : nvalid + (k - lo);
-      *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+  if (nvalid < kBs || lo > 0) {                                  // masked rows: zero the latent
+    if constexpr (kE4M3) {
+      for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 32; i += 256) {
+        const int k = i >> 5, ch = i & 31;
+        const int row = k < lo ? k : nvalid + (k - lo);
+        *(LDSP u32x4*)(buf + row * kRowC + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
+    } else {
+      for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 64; i += 256) {
+        const int k = i >> 6, ch = i & 63;
+        const int row = k < lo ? k : nvalid + (k - lo);
+        *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
+      }
     }
   }
   barrier_lds();                                                 // P^T, page maxima and flags visible
@@ -311,15 +328,40 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     asm volatile("s_nop 2" ::: "memory");                        // VALU -> MFMA source
   }
   const LDSP char* vbase = buf + ln.tr_off;
+  auto pload = [&](int ks, int h2) {
+    return *(const LDSP bf16x8*)(pt + (32 * h2 + ln.l32) * kPtRowB + (16 * ks + 8 * ln.hi) * 2);
+  };
+  if constexpr (kE4M3) {                 // V^T by transposed byte reads, converted before each MFMA pair
+    auto vraw = [&](int step) {
+      const int ks = step >> 2, cb = step & 3;
+      return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                           (LDSP i32x2*)(vbase + 16 * ks * kRowC + 32 * cb)));
+    };
+    u32x2 rcur = vraw(0);
+    bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
+    bf16x8 pn0 = pc0, pn1 = pc1;
+#pragma unroll
+    for (int step = 0; step < 16; ++step) {
+      const int cb = step & 3;
+      u32x2 rnext = rcur;
+      if (step + 1 < 16) rnext = vraw(step + 1);
+      if (cb == 0 && step + 4 < 16) { pn0 = pload((step >> 2) + 1, 0); pn1 = pload((step >> 2) + 1, 1); }
+      const bf16x8 v = cvt8(rcur);
+      asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n"
+                   "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
+                   : "+v"(acc.o[cb][0]), "+v"(acc.o[cb][1]) : "v"(v), "v"(pc0), "v"(pc1));
+      rcur = rnext;
+      if (cb == 3) { pc0 = pn0; pc1 = pn1; }
+    }
+    pg_after = pg2;
+    return;
+  }
   auto vload = [&](int step) {
     const int ks = step >> 2, cb = step & 3;
     const LDSP char* vp = vbase + 16 * ks * kRowB + 64 * cb;
     const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)vp);
     const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + kRowB));
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  auto pload = [&](int ks, int h2) {
-    return *(const LDSP bf16x8*)(pt + (32 * h2 + ln.l32) * kPtRowB + (16 * ks + 8 * ln.hi) * 2);
   };
   bf16x8 vcur = vload(0);
   bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
@@ -386,12 +428,21 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   {
     const int i = ln.l32, a = i >> 3, q = i & 3, bq = (i >> 2) & 1;
     const int tok = 32 * ln.th + 16 * (a >> 1) + 2 * (a & 1) + bq + 4 * q;
-    ln.a_off = tok * kRowB + ln.hi * 16;
+    ln.a_off = kE4M3 ? tok * kRowC + ln.hi * 8 : tok * kRowB + ln.hi * 16;
   }
   ln.pt_row = (ln.hb * 32 + ln.l32) * kPtRowB;
   {
     const int g = ln.lane >> 4, sg = ln.lane & 15;             // PV transposed reads
     ln.tr_off = (4 * (sg >> 2) + 2 * ln.hi) * kRowB + (128 * ln.wave + 16 * (g & 1) + 4 * (sg & 3)) * 2;
+    if (kE4M3) {
+      // transposed byte reads: within a 16-lane group, source lane sg names
+      // token row T(sg / 2) and the 8 codes at column 16 (g & 1) + 8 (sg & 1)
+      // of the wave's block; lane s then receives column 16 (g & 1) + s of
+      // rows T(0..7), the token order of the P^T slots 8 hi .. 8 hi + 7:
+      // T(e) = 4 (e & 3) + 2 hi + e / 4.
+      const int e = sg >> 1;
+      ln.tr_off = (4 * (e & 3) + 2 * ln.hi + (e >> 2)) * kRowC + 128 * ln.wave + 16 * (g & 1) + 8 * (sg & 1);
+    }
   }
 
   uint32_t offa[19];                                             // this lane's page-load offsets (AGPRs)
@@ -419,8 +470,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
     // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
-    // 1, both as whole 1 KiB direct loads.  E4M3: the queries go to the tile
-    // (buffer 0) and the first page's codes and scales to ring slot 0.
+    // 1, both as whole 1 KiB direct loads (an E4M3 page by its own walk).
     int32_t pg0, pg_next;
     Acc acc;                                                     // cleared while the first loads are in flight
 #pragma unroll
@@ -433,7 +483,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     acc.l_own = 0.f;
     {                                                            // queries first: they need no page id
       const char* qsrc_u = uniform(reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD));
-      const uint32_t q_m0 = uniform_lds(kE4M3 ? (LDSP char*)g_page0 : (LDSP char*)g_page1);
+      const uint32_t q_m0 = uniform_lds((LDSP char*)g_page1);
 #pragma unroll
       for (int i = 0; i < 19; ++i)
         if (i < ndma) dma16_u(qsrc_u, offa[i], q_m0 + 1024 * (ln.wave + 4 * i));
@@ -442,13 +492,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       sload2_i32(bt + jp0, bt + (jp0 + 1 < jp1 ? jp0 + 1 : jp0), &pg0, &pg_next);
       const char* src_u = uniform(cbase + (int64_t)pg0 * kPageBytesG);
       if constexpr (kE4M3) {
-        const uint32_t p_m0 = uniform_lds((LDSP char*)g_page1);
-#pragma unroll
-        for (int i = 0; i < 9; ++i) {
-          const uint32_t k = static_cast<uint32_t>(ln.wave + 4 * i);
-          dma16_u(src_u, 1024u * k + 16u * ln.lane, p_m0 + 1024u * k);
-        }
-        if (ln.wave == 0) dma4(sbase + (int64_t)pg0 * (kBs * 4), 4 * ln.lane, (LDSP char*)g_page1 + kCodesB);
+        dma_code_page(src_u, uniform_lds((LDSP char*)g_page0), sbase + (int64_t)pg0 * (kBs * 4),
+                      (LDSP char*)g_page0 + kCodeRowsB, ln.wave, ln.lane);
       } else {
         const uint32_t p_m0 = uniform_lds((LDSP char*)g_page0);
 #pragma unroll
@@ -460,7 +505,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     // direct loads complete in order): the first page keeps landing while
     // the queries are read into registers; its own wait is at the page top.
     if constexpr (kE4M3) {
-      if (ln.wave == 0) asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+      if (ln.wave == 0) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
       else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     } else {
       if (ndma == 19) asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
@@ -470,8 +515,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     // Q^T fragments stay in AGPRs for the whole segment (the MFMAs read them there)
     bf16x8 qf[36];
     {
-      const LDSP char* qrow = (kE4M3 ? (LDSP char*)g_page0 : (LDSP char*)g_page1) +
-                              (ln.hb * 32 + ln.l32) * kRowB + ln.hi * 16;
+      const LDSP char* qrow = (LDSP char*)g_page1 + (ln.hb * 32 + ln.l32) * kRowB + ln.hi * 16;
       bf16x8 t[36];
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) t[kb] = *(const LDSP bf16x8*)(qrow + 32 * kb);
@@ -492,15 +536,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
       const int nvalid = min(kBs, Lu - jp * kBs);                 // jp * 64 < L: no overflow
       const bool more = jp + 1 < j1;
-      if constexpr (kE4M3) {
-        LDSP char* cur = (LDSP char*)g_page1 + (even ? 0 : kCodeSlotB);
-        LDSP char* nxt = (LDSP char*)g_page1 + (even ? kCodeSlotB : 0);
-        page_step<true>(ln, (LDSP char*)g_page0, nxt, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next,
-                        offa, qf, nvalid, jp == 0 ? lo : 0, s2, acc, cur, sbase);
-      } else {
-        page_step<false>(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
-                         nvalid, jp == 0 ? lo : 0, s2, acc);
-      }
+      page_step<kE4M3>(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
+                       nvalid, jp == 0 ? lo : 0, s2, acc, sbase);
     }
 
     // ---- segment epilogue: normalise and store ------------------------------
