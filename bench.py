@@ -220,10 +220,12 @@ def main():
     if dec_us is None:                   # graph replay: the decode call is timed in the eager pass
         dec_us = call_us["decode"]
 
-    kvp = mq = None
+    kvp = mq = e8 = None
     if not args.no_extras:
         kvp = kv_project_measure(mla, d, w, dev, B, args.min_replica_mb)
         mq = multi_query_measure(mla, d, w, dev, reps, bt, lens, act, iters=20)
+        if w.kv == "bf16" and w.act == "bf16" and w.n_h % 64 == 0:
+            e8 = e4m3_measure(mla, w, dev, t_hist, cur, q_abs, bt, lens, args.min_replica_mb)
 
     # algorithmic work of one decode call
     toks = int(w.lens.sum())
@@ -268,6 +270,7 @@ def main():
         "cache_fill_GBps": round(cache_bytes / (np.median(fill_ms) * 1e-3) / 1e9, 1),
         "kv_project": kvp,
         "multi_query": mq,
+        "e4m3_cache": e8,
     }
 
     if not args.no_cpu:
@@ -327,6 +330,51 @@ def kv_project_measure(mla, d, w, dev, T, min_mb, d_model=5120, iters=50):
     return {"tokens": T, "d_model": d_model, "us": round(us, 3), "algorithmic_bytes": nbytes,
             "GBps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4), "weight_copies": R,
             "launch": "graph"}
+
+
+def e4m3_measure(mla, w, dev, t_hist, cur, q_abs, bt, lens, min_mb, iters=50):
+    """The same decode call with the cache stored as E4M3 rows and one float32
+    scale per row (same history and current rows, same queries): mean call
+    time over replicas rotated per call, and the rate against the bf16 MFMA
+    peak, which bounds it (the arithmetic runs on bf16 MFMA after exact code
+    conversion: 2 n_h (576 + 512) flops per 580-byte row, 480 flop/B at 128
+    heads, above the ridge)."""
+    import torch
+    B, nh, D = w.B, w.n_h, w.D
+    d8 = mla.make_dims(nh, w.d_h, w.d_c, w.d_R, w.block_size, act=w.act, kv="e4m3",
+                       softmax_scale=w.scale, rope_base=w.rope_base)
+    row = D + 4
+    cache_bytes = w.num_pages * w.block_size * row
+    R = max(2, math.ceil(min_mb * 1e6 / cache_bytes))
+    reps = []
+    for _ in range(R):
+        c = torch.zeros((w.num_pages, w.block_size, D), dtype=torch.uint8, device=dev)
+        sc = torch.ones((w.num_pages, w.block_size), dtype=torch.float32, device=dev)
+        mla.cache_append(d8, *t_hist, c, sc)
+        mla.cache_append(d8, *cur, c, sc)
+        reps.append((c, sc))
+    ws = torch.empty(mla.decode_workspace_bytes(d8, B, 0), dtype=torch.uint8, device=dev)
+    o = torch.empty((B, nh, w.d_c), dtype=q_abs.dtype, device=dev)
+    l = torch.empty((B, nh), dtype=torch.float32, device=dev)
+    for i in range(3):
+        mla.decode(d8, q_abs, reps[i % R][0], bt, lens, kv_scale=reps[i % R][1], workspace=ws, o_lat=o, lse=l)
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for i in range(iters):
+        evs[i][0].record(stream)
+        mla.decode(d8, q_abs, reps[i % R][0], bt, lens, kv_scale=reps[i % R][1], workspace=ws, o_lat=o, lse=l)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in evs]) * 1e3)
+    toks = int(w.lens.sum())
+    flops = toks * (2 * nh * D + 2 * nh * w.d_c)
+    nbytes = toks * row + B * nh * D * 2 + B * nh * w.d_c * 2 + B * nh * 4
+    tfl = flops / (us * 1e-6) / 1e12
+    return {"kv_dtype": "e4m3", "us": round(us, 3), "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "bound": "mfma", "TFLOPs": round(tfl, 1), "frac": round(tfl / BF16_PEAK_TFLOPS, 4),
+            "GBps": round(nbytes / (us * 1e-6) / 1e9, 1), "replicas": R,
+            "traffic": stored_traffic(w.name + "_e4m3")}
 
 
 def multi_query_measure(mla, d, w, dev, reps, bt, lens, act, q_len=4, iters=20):
