@@ -164,8 +164,9 @@ def test_generic_merge_few_and_many_parts(splits):
     _check_all(w, res)
 
 
-@pytest.mark.parametrize("n_h,splits", [(64, 0), (64, 37), (16, 0)])
-def test_batch_larger_than_a_workgroup(n_h, splits):
+@pytest.mark.parametrize("name,n_h,splits", [("v2_b16_4k", 64, 0), ("v2_b16_4k", 64, 37), ("v2_b16_4k", 16, 0),
+                                             ("v2_b16_4k_e4m3", 64, 0)])
+def test_batch_larger_than_a_workgroup(name, n_h, splits):
     """More sequences than threads in a workgroup (the part locators then sum
     several sequences per thread), with empty and one-token sequences among
     them; a sample of sequences is checked."""
@@ -173,7 +174,7 @@ def test_batch_larger_than_a_workgroup(n_h, splits):
     lens = rng.integers(0, 200, size=300)
     lens[[5, 6, 150]] = 0
     lens[[7, 299]] = 1
-    w = W.make("v2_b16_4k", B=300, lens=lens, n_h=n_h, shuffle=True)
+    w = W.make(name, B=300, lens=lens, n_h=n_h, shuffle=True)
     res = C.run_chain(w, num_splits=splits)
     seqs = [0, 5, 7, 8, 149, 150, 151, 298, 299]
     for b in seqs:
