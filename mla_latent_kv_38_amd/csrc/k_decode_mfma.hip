@@ -1,5 +1,10 @@
 // MFMA decode for DeepSeek-V2 shapes: d_c = 512, d_R = 64 (rows of 576),
-// 64-token pages, bfloat16 queries and cache, n_h a multiple of 64.
+// 64-token pages, bfloat16 queries, a bfloat16 or E4M3 cache, n_h a
+// multiple of 64.  Source: keybo.xyz page, section "第二步，推理时的吸收"
+// (scores against the cached latent with the absorbed query, softmax, the
+// weighted latent sum) and dgblog.top page, section "3. 一个聪明的优化：上采样
+// 矩阵可以"吸收""; the E4M3 row is code x per-row scale, which factors out of
+// both contractions.
 //
 // Work decomposition.  The batch's pages are flattened and cut into parts
 // (see mla_device.h); one workgroup handles one part for 64 heads.  A
@@ -21,6 +26,10 @@
 // 16-B column per phase) and the transposed PV reads (4 rows 4 apart x 32
 // columns per phase) are free of bank conflicts; the token order inside each
 // MFMA is permuted to match (it is a contraction index, so any order is exact).
+// E4M3 cache (decode_mfma_h64<true>): the same decomposition on code rows
+// padded to 592 B; QK reads 8-code groups and PV reads V^T with
+// ds_read_b64_tr_b8, each converted exactly to bf16 in registers before its
+// MFMA; the row scale multiplies the scores and P.
 #include "mla_device.h"
 #include "mla_internal.h"
 
