@@ -57,11 +57,18 @@ TRAFFIC_SOURCES = ["mla_latent_kv_38_amd/csrc/k_decode_mfma.hip", "mla_latent_kv
 
 
 def source_hash(paths):
+    """Hash of the code in the given C++ sources: comments and whitespace are
+    left out, so that only a change to the code itself retires a stored
+    measurement."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for rel in paths:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
