@@ -132,17 +132,24 @@ __device__ __forceinline__ void dma_code_page(const char* src_u, uint32_t dst_u,
 }
 
 // S^T for one wave from an E4M3 page: as qk_page, with each 8-code A
-// fragment converted in registers just before its MFMA.
+// fragment converted in registers just before its MFMA.  A lane reads 16
+// codes at a time (row tok, bytes 32 j + 16 hi), the fragments of MFMAs
+// 2 j and 2 j + 1, so the contraction index of MFMA 2 j + e2, lane half hi,
+// element e is 32 j + 16 hi + 8 e2 + e (the query fragments follow the same
+// order).  The 16-byte reads of 16 token rows 592 B apart cover all 64
+// banks once; 8-byte reads would meet 2-way conflicts.
 __device__ __forceinline__ f32x16 qk_page_e4m3(const LDSP char* __restrict__ ap, const bf16x8 (&qf)[36]) {
   f32x16 S;
-  constexpr int kPre = 4;
-  u32x2 cf[kPre];
+  constexpr int kPre = 2;                       // 16-code reads in flight (4 MFMAs)
+  u32x4 cf[kPre];
 #pragma unroll
-  for (int kb = 0; kb < kPre; ++kb) cf[kb] = *(const LDSP u32x2*)(ap + 16 * kb);
+  for (int j = 0; j < kPre; ++j) cf[j] = *(const LDSP u32x4*)(ap + 32 * j);
 #pragma unroll
   for (int kb = 0; kb < 36; ++kb) {
-    const bf16x8 a = cvt8(cf[kb % kPre]);
-    if (kb + kPre < 36) cf[kb % kPre] = *(const LDSP u32x2*)(ap + 16 * (kb + kPre));
+    const int j = kb >> 1;
+    const u32x4 w = cf[j % kPre];
+    const bf16x8 a = (kb & 1) ? cvt8(u32x2{w[2], w[3]}) : cvt8(u32x2{w[0], w[1]});
+    if ((kb & 1) && j + kPre < 18) cf[j % kPre] = *(const LDSP u32x4*)(ap + 32 * (j + kPre));
     if (kb == 0)
       asm volatile("s_nop 1\n v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(S) : "v"(a), "a"(qf[0]));
     else
@@ -437,7 +444,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   {
     const int i = ln.l32, a = i >> 3, q = i & 3, bq = (i >> 2) & 1;
     const int tok = 32 * ln.th + 16 * (a >> 1) + 2 * (a & 1) + bq + 4 * q;
-    ln.a_off = kE4M3 ? tok * kRowC + ln.hi * 8 : tok * kRowB + ln.hi * 16;
+    ln.a_off = kE4M3 ? tok * kRowC + ln.hi * 16 : tok * kRowB + ln.hi * 16;
   }
   ln.pt_row = (ln.hb * 32 + ln.l32) * kPtRowB;
   {
@@ -524,10 +531,12 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     // Q^T fragments stay in AGPRs for the whole segment (the MFMAs read them there)
     bf16x8 qf[36];
     {
-      const LDSP char* qrow = (LDSP char*)g_page1 + (ln.hb * 32 + ln.l32) * kRowB + ln.hi * 16;
+      const LDSP char* qrow = (LDSP char*)g_page1 + (ln.hb * 32 + ln.l32) * kRowB;
       bf16x8 t[36];
 #pragma unroll
-      for (int kb = 0; kb < 36; ++kb) t[kb] = *(const LDSP bf16x8*)(qrow + 32 * kb);
+      for (int kb = 0; kb < 36; ++kb)               // contraction order of qk_page / qk_page_e4m3
+        t[kb] = *(const LDSP bf16x8*)(qrow + (kE4M3 ? 64 * (kb >> 1) + 32 * ln.hi + 16 * (kb & 1)
+                                                    : 32 * kb + 16 * ln.hi));
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) asm volatile("" : "=a"(qf[kb]) : "0"(t[kb]));
     }
