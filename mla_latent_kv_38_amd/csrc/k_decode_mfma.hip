@@ -197,7 +197,7 @@ __shared__ __attribute__((aligned(16))) float g_xa[64];       // alpha per head
 __shared__ __attribute__((aligned(16))) float g_xl[2 * 64];   // row sums per token half
 __shared__ __attribute__((aligned(16))) float g_xf[64];       // final reference max
 __shared__ int32_t g_lens[256];                               // seq_lens, when the batch has <= 256
-__shared__ int32_t g_xneed[4];                                // per wave: its page half needs a new reference
+__shared__ __attribute__((aligned(16))) int32_t g_xneed[4];   // per wave: its page half needs a new reference
 
 struct Lane {                      // per-lane constants
   int wave, lane, l32, hi, hb, th, hg_part;
@@ -320,7 +320,31 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     }
   }
   barrier_lds();                                                 // P^T, page maxima and flags visible
-  const bool slow = (g_xneed[0] | g_xneed[1] | g_xneed[2] | g_xneed[3]) != 0;
+  // The flags and the first PV operands in one LDS round trip: the flags are
+  // read first (LDS reads return in order), V^T and P^T of step 0 behind them.
+  const LDSP char* vbase = buf + ln.tr_off;
+  auto pload = [&](int ks, int h2) {
+    return *(const LDSP bf16x8*)(pt + (32 * h2 + ln.l32) * kPtRowB + (16 * ks + 8 * ln.hi) * 2);
+  };
+  auto vraw = [&](int step) {            // E4M3: V^T by transposed byte reads
+    const int ks = step >> 2, cb = step & 3;
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                                         (LDSP i32x2*)(vbase + 16 * ks * kRowC + 32 * cb)));
+  };
+  auto vload = [&](int step) {           // bf16: V^T by transposed 16-bit reads
+    const int ks = step >> 2, cb = step & 3;
+    const LDSP char* vp = vbase + 16 * ks * kRowB + 64 * cb;
+    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)vp);
+    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + kRowB));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+  const u32x4 flags = *(const LDSP u32x4*)g_xneed;
+  u32x2 rcur{};
+  bf16x8 vcur{};
+  if constexpr (kE4M3) rcur = vraw(0);
+  else vcur = vload(0);
+  bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
+  const bool slow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
   float alpha = 1.f;
   if (slow) {
     const float mpage = fmaxf(mloc, xm[(1 - ln.th) * 64 + ln.hb * 32 + ln.l32]);
@@ -331,6 +355,8 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     make_p();
     if (ln.th == 0 && ln.hi == 0) xa[ln.hb * 32 + ln.l32] = alpha;
     barrier_lds();                                               // P^T and alpha visible
+    pc0 = pload(0, 0);                                           // P^T was rewritten
+    pc1 = pload(0, 1);
   }
   acc.l_own = acc.l_own * alpha + ps;
 
@@ -343,18 +369,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
       for (int r = 0; r < 16; ++r) { acc.o[cb][0][r] *= al0; acc.o[cb][1][r] *= al1; }
     asm volatile("s_nop 2" ::: "memory");                        // VALU -> MFMA source
   }
-  const LDSP char* vbase = buf + ln.tr_off;
-  auto pload = [&](int ks, int h2) {
-    return *(const LDSP bf16x8*)(pt + (32 * h2 + ln.l32) * kPtRowB + (16 * ks + 8 * ln.hi) * 2);
-  };
-  if constexpr (kE4M3) {                 // V^T by transposed byte reads, converted before each MFMA pair
-    auto vraw = [&](int step) {
-      const int ks = step >> 2, cb = step & 3;
-      return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                                           (LDSP i32x2*)(vbase + 16 * ks * kRowC + 32 * cb)));
-    };
-    u32x2 rcur = vraw(0);
-    bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
+  if constexpr (kE4M3) {                 // V^T converted before each MFMA pair
     bf16x8 pn0 = pc0, pn1 = pc1;
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
@@ -372,15 +387,6 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     pg_after = pg2;
     return;
   }
-  auto vload = [&](int step) {
-    const int ks = step >> 2, cb = step & 3;
-    const LDSP char* vp = vbase + 16 * ks * kRowB + 64 * cb;
-    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)vp);
-    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + kRowB));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
-  bf16x8 vcur = vload(0);
-  bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
   bf16x8 pn0 = pc0, pn1 = pc1;
 #pragma unroll
   for (int step = 0; step < 16; ++step) {
