@@ -437,15 +437,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
-  const PartRange pr = locate_part(seq_lens, seq_starts, B, kBs, part, W, g_lens);
-  const int32_t chunk = pr.chunk;
-  auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
-  const int64_t x1 = pr.x1;
-  int64_t x = pr.x0;
-  if (x >= x1) return;
-  int32_t b = pr.b;
-  int64_t first = pr.first;
-
   // QK A operand: lane reads token row tok(l32) of its half, 16-B chunk hi of each k-step
   {
     const int i = ln.l32, a = i >> 3, q = i & 3, bq = (i >> 2) & 1;
@@ -467,9 +458,19 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     }
   }
 
+  // (these do not depend on the part: computed while the locator's load is in flight)
   uint32_t offa[19];                                             // this lane's page-load offsets (AGPRs)
   dma_offsets(ln.wave, ln.lane, offa);
   const int ndma = dma_count(ln.wave);
+
+  const PartRange pr = locate_part(seq_lens, seq_starts, B, kBs, part, W, g_lens);
+  const int32_t chunk = pr.chunk;
+  auto seq_len = [&](int32_t bb) { return chunk == 1 ? g_lens[bb] : seq_lens[bb]; };
+  const int64_t x1 = pr.x1;
+  int64_t x = pr.x0;
+  if (x >= x1) return;
+  int32_t b = pr.b;
+  int64_t first = pr.first;
   const char* cbase = reinterpret_cast<const char*>(cache);
   const char* sbase = reinterpret_cast<const char*>(kv_scale);
   constexpr int64_t kPageBytesG = kE4M3 ? (int64_t)kCodePageB : (int64_t)kBs * kD * 2;
