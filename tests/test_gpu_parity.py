@@ -142,6 +142,24 @@ def test_fp8_64_head_groups(n_h, lens, splits):
     _check_all(w, res)
 
 
+@pytest.mark.parametrize("name", ["v2_b16_4k", "v2_b16_4k_e4m3"])
+@pytest.mark.parametrize("n_h,splits", [(192, 0), (256, 11)])
+def test_64_head_kernel_three_and_four_head_groups(name, n_h, splits):
+    """Head counts of 3 and 4 x 64: the parts then carry 3 or 4 workgroups
+    each, on both caches; ragged lengths, automatic and forced splits."""
+    w = W.make(name, B=3, lens=[300, 1, 777], n_h=n_h, shuffle=True)
+    res = C.run_chain(w, num_splits=splits)
+    _check_all(w, res, heads=[0, 63, 64, n_h - 1])
+
+
+def test_fp8_64_head_long_sequence_many_parts():
+    """One 8192-token E4M3 sequence (128 pages) cut into 96 parts, next to a
+    short one: most parts hold a page or two of the long sequence."""
+    w = W.make("v2_b16_4k_e4m3", B=2, lens=[8192, 70], n_h=64, shuffle=True)
+    res = C.run_chain(w, num_splits=96)
+    _check_all(w, res, heads=[0, 31, 32, 63])
+
+
 def test_fp8_64_head_page_permutation_is_bitwise_invariant():
     import copy
     a = W.make("v2_b16_4k_e4m3", B=2, lens=[700, 300], n_h=64, shuffle=False)
