@@ -105,8 +105,9 @@ def test_page_permutation_is_bitwise_invariant():
         assert torch.equal(ra[k], rb[k]), k
 
 
-def test_run_to_run_deterministic():
-    w = W.make("ragged_b64", B=2, lens=[900, 77])
+@pytest.mark.parametrize("name,n_h", [("ragged_b64", None), ("v2_b16_4k_e4m3", 128), ("fp8_h16_b128", None)])
+def test_run_to_run_deterministic(name, n_h):
+    w = W.make(name, B=2, lens=[900, 77], n_h=n_h)
     r1 = C.run_chain(w, num_splits=6)
     r2 = C.run_chain(w, num_splits=6)
     for k in ("o_lat", "lse", "out", "q_abs"):
