@@ -386,10 +386,12 @@ def e4m3_measure(mla, w, dev, t_hist, cur, q_abs, bt, lens, min_mb, iters=50):
 
 def multi_query_measure(mla, d, w, dev, reps, bt, lens, act, q_len=4, iters=20):
     """mla_decode_multi with q_len new query tokens per sequence (the last
-    q_len rows of each sequence are theirs) on the same caches: mean call time
-    and the HBM rate on the algorithmic bytes (every latent row once, the
-    queries, the outputs).  Each query token reads its rows separately, so
-    the rate is at most 1/q_len of the one-query decode's."""
+    q_len rows of each sequence are theirs) on the same caches: mean call
+    time, the HBM rate on the algorithmic bytes (every latent row once, the
+    queries, the outputs) and the MFMA rate on the algorithmic flops (each
+    query over its own rows); `frac` is against whichever bounds the call
+    (at 128 heads and q_len 4 the flops per byte are above the bf16 ridge,
+    so the MFMA does)."""
     import torch
     B, nh, D = w.B, w.n_h, w.D
     gen = torch.Generator(device=dev).manual_seed(11)
@@ -416,9 +418,15 @@ def multi_query_measure(mla, d, w, dev, reps, bt, lens, act, q_len=4, iters=20):
     esz = 1 if w.kv == "e4m3" else (2 if w.kv == "bf16" else 4)
     asz = 2 if w.act == "bf16" else 4
     nbytes = int(w.lens.sum()) * (D * esz + (4 if w.kv == "e4m3" else 0)) + B * q_len * nh * (D + w.d_c) * asz
+    # query i of sequence b attends to its first L_b - q_len + 1 + i rows
+    rows = sum(max(0, int(L) - q_len + 1 + i) for L in w.lens for i in range(q_len))
+    flops = rows * (2 * nh * D + 2 * nh * w.d_c)
     gbps = nbytes / (us * 1e-6) / 1e9
-    return {"q_len": q_len, "us": round(us, 3), "algorithmic_bytes": nbytes, "GBps": round(gbps, 1),
-            "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+    tfl = flops / (us * 1e-6) / 1e12
+    mfma_bound = flops / nbytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    return {"q_len": q_len, "us": round(us, 3), "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+            "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1), "bound": "mfma" if mfma_bound else "hbm",
+            "frac": round(tfl / BF16_PEAK_TFLOPS if mfma_bound else gbps / HBM_PEAK_GBPS, 4)}
 
 
 def cpu_baseline(w, seconds, row_bytes):
