@@ -429,16 +429,20 @@ def multi_query_measure(mla, d, w, dev, reps, bt, lens, act, q_len=4, iters=20):
             "frac": round(tfl / BF16_PEAK_TFLOPS if mfma_bound else gbps / HBM_PEAK_GBPS, 4)}
 
 
-def cpu_baseline(w, seconds, row_bytes):
-    """The float64 oracle (explicit k_C / v reconstruction) timed on host cores
-    on a bounded sample of the same workload: whole sequences with all heads,
-    in batch order (wrapping round), until about `seconds` have passed."""
-    from oracle import mla_oracle as O
+def _cpu_model():
     try:
-        cores = len(os.sched_getaffinity(0))
-    except AttributeError:
-        cores = os.cpu_count()
-    threads = int(os.environ.get("OMP_NUM_THREADS", cores))
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def _oracle_rate(O, w, seconds):
+    """Whole-sequence oracle decodes in batch order (wrapping round) until
+    about `seconds` have passed; returns (sequences, tokens, seconds)."""
     nseq, toks = 0, 0
     t0 = time.perf_counter()
     while nseq == 0 or time.perf_counter() - t0 < seconds:
@@ -447,10 +451,46 @@ def cpu_baseline(w, seconds, row_bytes):
                           scale=w.scale, base=w.rope_base)
         nseq += 1
         toks += int(w.lens[b])
-    dt = time.perf_counter() - t0
-    return {"value": round(toks * row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": min(threads, cores),
-            "kind": "oracle", "sample": f"{nseq} sequence decodes of the {w.B}-sequence batch, in batch order "
-                                        f"({toks} tokens, all {w.n_h} heads), {dt:.2f} s"}
+    return nseq, toks, time.perf_counter() - t0
+
+
+def _tiny_one_thread(O, reps=200):
+    """The oracle on the tiny float32 workload (one 64-token sequence, 4 heads):
+    projections from the hidden states, then the explicit decode; mean time."""
+    import mla_inputs as W
+    t = W.make("tiny_f32")
+    r = t.raw
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        c_kv, k_r, q_c, q_r = O.project(r["h"], r["w_dkv"], r["w_kr"], r["w_q"], t.n_h, t.d_h, t.d_R)
+        O.explicit_decode(q_c, q_r, c_kv, k_r, r["w_uk"], r["w_uv"], scale=t.scale, base=t.rope_base)
+    us = (time.perf_counter() - t0) / reps * 1e6
+    return {"us_per_decode": round(us, 1), "tokens": int(t.lens[0]), "n_heads": t.n_h,
+            "GBps": round(int(t.lens[0]) * t.D * 4 / (us * 1e-6) / 1e9, 4)}
+
+
+def cpu_baseline(w, seconds, row_bytes):
+    """The float64 oracle (explicit k_C / v reconstruction) timed on host cores
+    on a bounded sample of the same workload: whole sequences with all heads,
+    in batch order (wrapping round), until about `seconds` have passed; then
+    the same with the BLAS pool held to one thread for a quarter of that."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    from oracle import mla_oracle as O
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    threads = max((int(p.get("num_threads", 1)) for p in blas), default=1)
+    nseq, toks, dt = _oracle_rate(O, w, seconds)
+    with threadpool_limits(limits=1, user_api="blas"):
+        n1, t1, dt1 = _oracle_rate(O, w, seconds / 4)
+        tiny = _tiny_one_thread(O)
+    return {"value": round(toks * row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "blas": [f"{p.get('internal_api')} {p.get('version')} x{p.get('num_threads')}" for p in blas],
+            "sample": f"{nseq} sequence decodes of the {w.B}-sequence batch, in batch order "
+                      f"({toks} tokens, all {w.n_h} heads), {dt:.2f} s",
+            "one_thread": {"value": round(t1 * row_bytes / dt1 / 1e9, 4), "unit": "GB/s",
+                           "sample": f"{n1} sequence decodes ({t1} tokens), {dt1:.2f} s, BLAS held to 1 thread"},
+            "one_thread_tiny_f32": tiny}
 
 
 if __name__ == "__main__":

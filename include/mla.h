@@ -36,6 +36,12 @@
  *     RoPE angles, cosines and sines are computed in float64.
  *   - The functions are stateless and may be called from several host threads
  *     (mla_last_hip_error is per thread).
+ *   - `stream` is a hipStream_t passed as void* so that this header needs no
+ *     HIP include; the caller casts.
+ *   - Decode calls take no maximum-length hint: the split-KV plan (how many
+ *     chunks, how much workspace) depends only on the batch size, the head
+ *     count and num_splits, and the kernels read the lengths themselves, so
+ *     the same workspace serves any lengths within the block table.
  */
 #ifndef MLA_H_
 #define MLA_H_
@@ -73,7 +79,8 @@ typedef struct mla_dims {
   int32_t act_dtype;     /* mla_dtype of q_c, q_r, c_kv, k_r, w_uk, w_uv, q_abs,
                             o_lat and out: MLA_F32 or MLA_BF16                  */
   int32_t kv_dtype;      /* cache element type: MLA_F32, MLA_BF16 or MLA_E4M3   */
-  float softmax_scale;   /* multiplies q_abs . row; normally 1/sqrt(d_h + d_R)  */
+  float softmax_scale;   /* multiplies q_abs . row; normally 1/sqrt(d_h + d_R);
+                            finite and > 0 (else MLA_ERR_SHAPE)               */
   double rope_base;      /* RoPE base b: theta_i = b^(-2i/d_R), pairs (2i, 2i+1) */
 } mla_dims;
 

@@ -25,7 +25,9 @@ mla_status check_dims(const mla_dims* d) {
   if (d->d_head > kMaxWidth || d->d_latent + d->d_rope > kMaxWidth || d->block_size > 4096)
     return MLA_ERR_SHAPE;
   if (!valid_dtype(d->act_dtype, false) || !valid_dtype(d->kv_dtype, true)) return MLA_ERR_DTYPE;
-  if (!isfinite(d->softmax_scale)) return MLA_ERR_SHAPE;
+  // The decode kernels take the running maximum of raw scores and apply the
+  // scale afterwards, which needs scale > 0 (a positive factor commutes with max).
+  if (!isfinite(d->softmax_scale) || !(d->softmax_scale > 0.f)) return MLA_ERR_SHAPE;
   if (d->d_rope > 0 && !(d->rope_base > 0.0 && isfinite(d->rope_base))) return MLA_ERR_SHAPE;
   return MLA_OK;
 }

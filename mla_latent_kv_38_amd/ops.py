@@ -3,11 +3,19 @@
 Argument marshalling only (dtype/shape/device checks, data pointers, the
 current HIP stream).  Every step of the computation runs in the HIP library;
 there is no CPU or PyTorch fallback.
+
+The library does not read device-resident indices on the host (slots, page
+ids, lengths): out-of-range values there are undefined behaviour on the GPU.
+Setting MLA_VALIDATE=1 in the environment makes the calls below copy those
+small index tensors to the host first and raise ValueError on any violation
+(`check_slots`, `check_paging`); this synchronises the stream and is meant
+for debugging.
 """
 from __future__ import annotations
 
 import ctypes
 import math
+import os
 
 import torch
 
@@ -48,6 +56,47 @@ def _need(t, name, dtype, shape=None):
     return t
 
 
+def _validating() -> bool:
+    return os.environ.get("MLA_VALIDATE", "") not in ("", "0")
+
+
+def check_slots(slot, num_pages: int, block_size: int):
+    """Host check of an append's slots: 0 <= slot < num_pages * block_size and
+    no slot twice (two rows written to one place in one call)."""
+    s = slot.detach().cpu().to(torch.int64)
+    cap = int(num_pages) * int(block_size)
+    bad = ((s < 0) | (s >= cap)).nonzero().flatten()
+    if bad.numel():
+        i = int(bad[0])
+        raise ValueError(f"slot[{i}] = {int(s[i])} outside [0, {cap})")
+    if torch.unique(s).numel() != s.numel():
+        raise ValueError("slots repeat within one call")
+
+
+def check_paging(block_table, seq_lens, num_pages: int, block_size: int, seq_starts=None):
+    """Host check of a decode's paging: 0 <= seq_starts[b] and
+    0 <= seq_lens[b] <= max_pages * block_size, and every block-table entry the
+    decode reads (pages seq_starts[b] // block_size .. ceil(L / block_size) - 1)
+    names a page in [0, num_pages)."""
+    bt = block_table.detach().cpu().to(torch.int64)
+    lens = seq_lens.detach().cpu().to(torch.int64)
+    starts = torch.zeros_like(lens) if seq_starts is None else seq_starts.detach().cpu().to(torch.int64)
+    max_pages = bt.shape[1]
+    for b in range(lens.numel()):
+        L, st = int(lens[b]), int(starts[b])
+        if L < 0 or L > max_pages * block_size:
+            raise ValueError(f"seq_lens[{b}] = {L} outside [0, {max_pages * block_size}]")
+        if st < 0:
+            raise ValueError(f"seq_starts[{b}] = {st} < 0")
+        if st >= L:
+            continue
+        used = bt[b, st // block_size:(L + block_size - 1) // block_size]
+        bad = ((used < 0) | (used >= num_pages)).nonzero().flatten()
+        if bad.numel():
+            k = st // block_size + int(bad[0])
+            raise ValueError(f"block_table[{b}, {k}] = {int(bt[b, k])} outside [0, {num_pages})")
+
+
 def _kv_torch(d: Dims):
     return (torch.uint8, torch.float8_e4m3fn) if d.kv_dtype == MLA_E4M3 else _TORCH[d.kv_dtype]
 
@@ -85,6 +134,8 @@ def cache_append(d: Dims, c_kv, k_r, pos, slot, kv_cache, kv_scale=None, stream=
         raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)}")
     if d.kv_dtype == MLA_E4M3:
         _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    if _validating():
+        check_slots(slot, kv_cache.shape[0], d.block_size)
     check(_lib.lib().mla_cache_append(ctypes.byref(d), T, _ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot),
                                       kv_cache.shape[0], _ptr(kv_cache), _ptr(kv_scale), _stream(stream)),
           "mla_cache_append")
@@ -116,6 +167,8 @@ def absorb_q_append(d: Dims, q_c, q_r, q_pos, w_uk, c_kv, k_r, pos, slot, kv_cac
         raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)}")
     if d.kv_dtype == MLA_E4M3:
         _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    if _validating():
+        check_slots(slot, kv_cache.shape[0], d.block_size)
     check(_lib.lib().mla_absorb_q_append(ctypes.byref(d), B, _ptr(q_c), _ptr(q_r), _ptr(q_pos), _ptr(w_uk),
                                          _ptr(q_abs), T, _ptr(c_kv), _ptr(k_r), _ptr(pos), _ptr(slot),
                                          kv_cache.shape[0], _ptr(kv_cache), _ptr(kv_scale), _stream(stream)),
@@ -144,6 +197,8 @@ def kv_project_append(d: Dims, h, w_dkv, w_kr, pos, slot, kv_cache, kv_scale=Non
         raise ValueError(f"kv_cache shape {tuple(kv_cache.shape)}")
     if d.kv_dtype == MLA_E4M3:
         _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    if _validating():
+        check_slots(slot, kv_cache.shape[0], d.block_size)
     need = kv_project_workspace_bytes(d, T, dm)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=h.device)
@@ -175,6 +230,8 @@ def decode(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None, num_s
         _need(seq_starts, "seq_starts", torch.int32, (B,))
     if d.kv_dtype == MLA_E4M3:
         _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    if _validating():
+        check_paging(block_table, seq_lens, kv_cache.shape[0], d.block_size, seq_starts)
     need = decode_workspace_bytes(d, B, num_splits)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)
@@ -216,6 +273,8 @@ def decode_multi(d: Dims, q_abs, kv_cache, block_table, seq_lens, kv_scale=None,
         _need(seq_starts, "seq_starts", torch.int32, (B,))
     if d.kv_dtype == MLA_E4M3:
         _need(kv_scale, "kv_scale", torch.float32, kv_cache.shape[:2])
+    if _validating():
+        check_paging(block_table, seq_lens, kv_cache.shape[0], d.block_size, seq_starts)
     need = int(_lib.lib().mla_decode_multi_workspace_bytes(ctypes.byref(d), B, q, num_splits))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q_abs.device)

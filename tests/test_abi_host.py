@@ -74,6 +74,12 @@ def test_validation_errors_launch_nothing():
     assert lib.mla_absorb_q(ref(bad), 4, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
     bad = _dims(rope_base=0.0)
     assert lib.mla_absorb_q(ref(bad), 4, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
+    for sc in (0.0, -0.125, float("inf"), float("nan")):       # softmax_scale must be finite and > 0
+        bad = _dims(softmax_scale=sc)
+        assert lib.mla_absorb_q(ref(bad), 4, FAKE, FAKE, FAKE, FAKE, FAKE, NULL) == -2
+        assert lib.mla_decode_workspace_bytes(ref(bad), 16, 0) == 0
+        assert lib.mla_decode(ref(bad), 16, FAKE, FAKE, NULL, FAKE, 64, FAKE, 0, ctypes.c_void_p(0x10000),
+                              1 << 40, FAKE, NULL, NULL) == -2
     # cache_append
     assert lib.mla_cache_append(ref(d), 0, NULL, NULL, NULL, NULL, 1, NULL, NULL, NULL) == 0  # no-op
     assert lib.mla_cache_append(ref(d), -1, FAKE, FAKE, FAKE, FAKE, 1, FAKE, NULL, NULL) == -2

@@ -1,8 +1,11 @@
 """GPU parity of the two projections around latent attention, element by
 element against the float64 oracle on the same bf16 inputs:
 
-  absorb_q   q_abs = [W_UK^T q_C || RoPE(q_R)]     (DeepSeek-V2 paper, sec. 2.1.2-2.1.3)
-  up_v       out   = W_UV o_lat                     (same section, absorbed W_UV)
+  absorb_q   q_abs = [W_UK^T q_C || RoPE(q_R)]     (keybo.xyz page, sections "第二步，推理时的吸收"
+                                                    and "RoPE 为什么必须解耦"; dgblog.top page,
+                                                    section "3. 一个聪明的优化")
+  up_v       out   = W_UV o_lat                     (keybo.xyz page, "第二步，推理时的吸收":
+                                                    one W_UV after the latent sum)
 
 A bf16 output is the exact value rounded once, after float32 accumulation of
 d_h (or d_c) products, so every element must satisfy

@@ -35,6 +35,52 @@ def test_worked_example_projection():
     assert c_kv.shape[1] == g["expected"]["cached_numbers_after"]
 
 
+def test_project_unit_hidden_states_pick_weight_columns():
+    """h_j = e_(k_j) (one-hot rows): c_kv[j] is column k_j of W_DKV, the raw
+    RoPE key k_r[j] is column k_j of W_KR, and the query of the last token is
+    column k_(L-1) of W_Q read as [n_h, d_h + d_R]: its first d_h entries per
+    head are q_C, the remaining d_R are q_R.  Checked entry by entry with
+    scalar indexing."""
+    rng = np.random.default_rng(21)
+    n_h, d_h, d_r, d_c, dm = 3, 4, 2, 5, 7
+    w_dkv = rng.standard_normal((d_c, dm))
+    w_kr = rng.standard_normal((d_r, dm))
+    w_q = rng.standard_normal((n_h * (d_h + d_r), dm))
+    ks = [3, 0, 6, 2]
+    h = np.zeros((len(ks), dm))
+    for j, k in enumerate(ks):
+        h[j, k] = 1.0
+    c_kv, k_r, q_c, q_r = O.project(h, w_dkv, w_kr, w_q, n_h, d_h, d_r)
+    for j, k in enumerate(ks):
+        for c in range(d_c):
+            assert c_kv[j, c] == w_dkv[c, k]
+        for i in range(d_r):
+            assert k_r[j, i] == w_kr[i, k]
+    kq = ks[-1]
+    for hh in range(n_h):
+        for i in range(d_h):
+            assert q_c[hh, i] == w_q[hh * (d_h + d_r) + i, kq]
+        for i in range(d_r):
+            assert q_r[hh, i] == w_q[hh * (d_h + d_r) + d_h + i, kq]
+
+
+def test_project_is_linear_in_the_hidden_state():
+    """Two one-hot rows added give the sum of their columns (the map is the
+    matrix product, nothing else)."""
+    rng = np.random.default_rng(22)
+    n_h, d_h, d_r, d_c, dm = 2, 3, 2, 4, 5
+    w_dkv, w_kr = rng.standard_normal((d_c, dm)), rng.standard_normal((d_r, dm))
+    w_q = rng.standard_normal((n_h * (d_h + d_r), dm))
+    h = np.zeros((1, dm))
+    h[0, 1], h[0, 4] = 2.0, -3.0
+    c_kv, k_r, q_c, q_r = O.project(h, w_dkv, w_kr, w_q, n_h, d_h, d_r)
+    np.testing.assert_allclose(c_kv[0], 2 * w_dkv[:, 1] - 3 * w_dkv[:, 4], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(k_r[0], 2 * w_kr[:, 1] - 3 * w_kr[:, 4], rtol=0, atol=1e-14)
+    q = (2 * w_q[:, 1] - 3 * w_q[:, 4]).reshape(n_h, d_h + d_r)
+    np.testing.assert_allclose(q_c, q[:, :d_h], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(q_r, q[:, d_h:], rtol=0, atol=1e-14)
+
+
 def test_worked_example_single_token_attends_to_its_value():
     """With one cached token the softmax weight is 1, so out = v exactly."""
     g = _golden()
@@ -374,6 +420,26 @@ def test_empty_sequence():
 # ---------------------------------------------------------------------------
 # Paging (keybo.xyz, "所以 cache 逻辑到底哪里要重写": paged by token latent)
 # ---------------------------------------------------------------------------
+def test_slot_of_hand_computed_table():
+    """Block-table row [2, 0, 1] with 4-token pages: logical token j lives in
+    physical page row[j // 4] at offset j % 4, so its slot is
+    4 * row[j // 4] + j % 4.  The table below is written out by hand."""
+    row = [2, 0, 1]
+    expected = {0: 8, 1: 9, 3: 11, 4: 0, 5: 1, 7: 3, 8: 4, 9: 5, 11: 7}
+    for j, slot in expected.items():
+        assert O.slot_of(row, j, 4) == slot
+
+
+def test_gather_pages_hand_computed_rows():
+    """A pool whose entry (page p, offset o) holds the value 10 p + o: reading
+    row [2, 0, 1] for 6 tokens gives pages 2 then 0, offsets 0..3 then 0..1."""
+    pool = np.array([[[10.0 * p + o] for o in range(4)] for p in range(3)])
+    got = O.gather_pages(pool, [2, 0, 1], 6)[:, 0].tolist()
+    assert got == [20.0, 21.0, 22.0, 23.0, 0.0, 1.0]
+    got = O.gather_pages(pool, [1, 2, 0], 9)[:, 0].tolist()
+    assert got == [10.0, 11.0, 12.0, 13.0, 20.0, 21.0, 22.0, 23.0, 0.0]
+
+
 def test_paged_gather_is_exact_under_any_page_table():
     rng = np.random.default_rng(8)
     bs, D, L = 4, 6, 13
@@ -430,9 +496,41 @@ def _mutant_window_off_by_one(q_c, q_r, c_kv, k_r, w_uk, w_uv, *, start, scale, 
                              q_pos=L - 1, k_pos=np.arange(start + 1, L), **kw)
 
 
+def _mutant_slot_of_swapped(block_table_row, j, block_size):
+    # page and offset exchanged: the offset scaled, the page added
+    return (j % block_size) * block_size + int(block_table_row[j // block_size])
+
+
+def _mutant_gather_pages_logical(pool, block_table_row, L):
+    pool = np.asarray(pool)
+    bs = pool.shape[1]
+    idx = np.arange(L)
+    return pool[idx // bs, idx % bs]          # block table ignored
+
+
+def _mutant_project_split_swapped(h, w_dkv, w_kr, w_q, n_heads, d_head, d_rope):
+    h = np.asarray(h, float)
+    c_kv = h @ np.asarray(w_dkv, float).T
+    k_r_raw = h @ np.asarray(w_kr, float).T if d_rope else np.zeros((h.shape[0], 0))
+    q = (np.asarray(w_q, float) @ h[-1]).reshape(n_heads, d_head + d_rope)
+    return c_kv, k_r_raw, q[:, d_rope:].copy(), q[:, :d_rope].copy()   # RoPE part taken first
+
+
+def _mutant_project_kr_first_token(h, w_dkv, w_kr, w_q, n_heads, d_head, d_rope):
+    h = np.asarray(h, float)
+    c_kv = h @ np.asarray(w_dkv, float).T
+    k_r_raw = np.repeat(h[:1] @ np.asarray(w_kr, float).T, h.shape[0], axis=0)   # every row from token 0
+    q = (np.asarray(w_q, float) @ h[-1]).reshape(n_heads, d_head + d_rope)
+    return c_kv, k_r_raw, q[:, :d_head].copy(), q[:, d_head:].copy()
+
+
 @pytest.mark.parametrize("name,mutant", [("rope", _mutant_rope_half_split),
                                          ("up_project", _mutant_up_project_transposed),
-                                         ("window_decode", _mutant_window_off_by_one)])
+                                         ("window_decode", _mutant_window_off_by_one),
+                                         ("slot_of", _mutant_slot_of_swapped),
+                                         ("gather_pages", _mutant_gather_pages_logical),
+                                         ("project", _mutant_project_split_swapped),
+                                         ("project", _mutant_project_kr_first_token)])
 def test_pins_catch_planted_mistakes(monkeypatch, name, mutant):
     monkeypatch.setattr(O, name, mutant)
     with pytest.raises(AssertionError):
@@ -441,5 +539,11 @@ def test_pins_catch_planted_mistakes(monkeypatch, name, mutant):
         elif name == "rope":
             test_rope_closed_forms()
             test_brute_force_matches_oracle(2, 3, 4, 4, 6)
+        elif name == "slot_of":
+            test_slot_of_hand_computed_table()
+        elif name == "gather_pages":
+            test_gather_pages_hand_computed_rows()
+        elif name == "project":
+            test_project_unit_hidden_states_pick_weight_columns()
         else:
             test_worked_example_projection()
