@@ -252,6 +252,35 @@ mla_status mla_decode_window(const mla_dims* dims, int32_t batch, const void* q_
                              void* workspace, size_t workspace_bytes, void* o_lat, float* lse, void* stream);
 
 /*
+ * mla_decode_noalloc - mla_decode_window without a caller workspace, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).
+ *
+ *   Computes exactly what mla_decode_window computes with the same arguments
+ *   (the same kernels; seq_starts may be NULL, which is mla_decode), keeping
+ *   the split-KV partials in a scratch array built into the library:
+ *   MLA_NOALLOC_SCRATCH_BYTES of device memory per GPU, held from the moment
+ *   the library's device code is loaded on that GPU until the process ends.
+ *   The call allocates and frees nothing; the caller still provides every
+ *   input and output.
+ *
+ *   Limit: mla_decode_workspace_bytes(dims, batch, num_splits) must not
+ *   exceed MLA_NOALLOC_SCRATCH_BYTES, else MLA_ERR_WORKSPACE and nothing is
+ *   launched.  (At 128 heads and automatic splits that covers batches of 96 sequences.)
+ *   No part of the scratch needs to start at any value: the kernels write
+ *   every byte they read within the call.
+ *   Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ *   one GPU (different streams, or different host threads without ordering)
+ *   race and must be serialised by the caller.
+ *   Errors: as mla_decode_window, with MLA_ERR_WORKSPACE for the limit.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t batch, const void* q_abs, const void* kv_cache,
+                              const float* kv_scale, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, const int32_t* seq_starts, int32_t num_splits, void* o_lat,
+                              float* lse, void* stream);
+
+/*
  * mla_decode_multi_workspace_bytes - device workspace mla_decode_multi needs.
  * Pure host computation; returns 0 when the arguments are invalid.
  */

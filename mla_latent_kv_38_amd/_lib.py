@@ -9,6 +9,7 @@ from .build import LIB_PATH
 c_int32, c_int64, c_void_p, c_size_t = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t
 
 MLA_F32, MLA_BF16, MLA_E4M3 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20     # MLA_NOALLOC_SCRATCH_BYTES
 
 STATUS = {0: "MLA_OK", -1: "MLA_ERR_NULL", -2: "MLA_ERR_SHAPE", -3: "MLA_ERR_DTYPE",
           -4: "MLA_ERR_WORKSPACE", -5: "MLA_ERR_UNSUPPORTED", -6: "MLA_ERR_HIP"}
@@ -29,6 +30,8 @@ SIGNATURES = {
                              c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
     "mla_decode_window": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                                     c_void_p, c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),
+    "mla_decode_noalloc": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
+                                     c_void_p, c_int32, c_void_p, c_void_p, c_void_p]),
     "mla_decode_multi_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32, c_int32]),
     "mla_decode_multi": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32,
                                    c_void_p, c_void_p, c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),

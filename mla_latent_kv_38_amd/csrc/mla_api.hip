@@ -3,9 +3,42 @@
 // machine without a GPU).
 #include <math.h>
 
+#include <mutex>
+
 #include "mla_internal.h"
 
 namespace {
+
+// ---- the no-allocation decode's scratch -------------------------------------
+// mla_decode_noalloc keeps its split-KV workspace in this array instead of a
+// caller buffer.  Every GPU the library runs on holds its own copy (its own
+// address) from module load until the process ends.  In host code `scratch`
+// is only a stand-in for the symbol: its device address is looked up once
+// per device with hipGetSymbolAddress and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call for that device, with it current).
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 thread_local int32_t g_last_hip_error = 0;
 
@@ -110,6 +143,24 @@ mla_status mla_decode_window(const mla_dims* dims, int32_t batch, const void* q_
   return hip_status(mla::launch_decode(*dims, plan, batch, q_abs, kv_cache, kv_scale, block_table,
                                        max_pages, 1, seq_lens, seq_starts, workspace, o_lat, lse,
                                        static_cast<hipStream_t>(stream)));
+}
+
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t batch, const void* q_abs, const void* kv_cache,
+                              const float* kv_scale, const int32_t* block_table, int32_t max_pages,
+                              const int32_t* seq_lens, const int32_t* seq_starts, int32_t num_splits, void* o_lat,
+                              float* lse, void* stream) {
+  mla_status st = check_dims(dims);
+  if (st != MLA_OK) return st;
+  if (batch < 1 || max_pages < 1 || num_splits < 0 || num_splits > 65536) return MLA_ERR_SHAPE;
+  if (!q_abs || !kv_cache || !block_table || !seq_lens || !o_lat) return MLA_ERR_NULL;
+  if (dims->kv_dtype == MLA_E4M3 && !kv_scale) return MLA_ERR_NULL;
+  const mla::DecodePlan plan = mla::plan_decode(*dims, batch, num_splits);
+  if (plan.ws_bytes > kScratchBytes) return MLA_ERR_WORKSPACE;   // checked before any HIP call
+  void* ws = nullptr;
+  hipError_t e = scratch_on_current_device(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(mla::launch_decode(*dims, plan, batch, q_abs, kv_cache, kv_scale, block_table, max_pages, 1,
+                                       seq_lens, seq_starts, ws, o_lat, lse, static_cast<hipStream_t>(stream)));
 }
 
 size_t mla_decode_multi_workspace_bytes(const mla_dims* dims, int32_t batch, int32_t q_len, int32_t num_splits) {

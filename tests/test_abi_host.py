@@ -108,6 +108,16 @@ def test_validation_errors_launch_nothing():
                                  FAKE, NULL, NULL) == -1
     assert lib.mla_decode_window(ref(d), 16, FAKE, FAKE, NULL, FAKE, 0, FAKE, NULL, 0, ws, need,
                                  FAKE, NULL, NULL) == -2
+    # decode_noalloc: same validation as decode_window; a plan beyond the built-in scratch is refused
+    nargs = [FAKE, FAKE, NULL, FAKE, 64, FAKE, NULL, 0]
+    assert lib.mla_decode_noalloc(ref(d), 0, *nargs, FAKE, NULL, NULL) == -2
+    assert lib.mla_decode_noalloc(ref(d), 16, *nargs, NULL, NULL, NULL) == -1
+    assert lib.mla_decode_noalloc(ref(d8), 16, *nargs, FAKE, NULL, NULL) == -1        # no kv_scale
+    big = 1
+    while lib.mla_decode_workspace_bytes(ref(d), big, 0) <= L.NOALLOC_SCRATCH_BYTES:
+        big *= 2
+    assert lib.mla_decode_noalloc(ref(d), big, *nargs, FAKE, NULL, NULL) == -4
+    assert lib.mla_decode_workspace_bytes(ref(d), 96, 0) <= L.NOALLOC_SCRATCH_BYTES   # the header's stated cover
     # kv_project_append
     pw = lib.mla_kv_project_workspace_bytes(ref(d), 16, 5120)
     assert pw >= 16 * 576 * 4
