@@ -561,6 +561,9 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
   const bool aligned = (reinterpret_cast<uintptr_t>(q_abs) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(cache) % 16 == 0) &&
                        (reinterpret_cast<uintptr_t>(o_lat) % 8 == 0);
+  if (plan.kernel == kDecodeH64 && aligned && h64w_decode_supported(d))
+    return launch_decode_h64w(d, plan, B, q_abs, cache, block_table, max_pages, bt_div, seq_lens, seq_starts, ws_o,
+                              ws_lse, ws_tbl, o_lat, lse, s);
   if (plan.kernel == kDecodeH64 && aligned &&
       (d.kv_dtype != MLA_E4M3 || reinterpret_cast<uintptr_t>(kv_scale) % 4 == 0))
     return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,

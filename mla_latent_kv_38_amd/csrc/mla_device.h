@@ -179,9 +179,19 @@ __device__ __forceinline__ void sload2_i32(const int32_t* p, const int32_t* q, i
 // pages of its window, see window_pages below) and cut into `parts` contiguous
 // ranges: part w covers [floor(w P / W), floor((w+1) P / W)).  A (part,
 // sequence) overlap is a segment; its partial result lives in slot w + b.
-__device__ __forceinline__ int64_t part_start(int64_t w, int64_t P, int64_t W) { return (w * P) / W; }
+// floor(a / b) for 0 <= a < 2^53 and 1 <= b < 2^31: the float64 quotient is
+// within one of it and is corrected to the exact value (cheaper than the
+// 64-bit integer division routine).
+__device__ __forceinline__ int64_t div_floor53(int64_t a, int64_t b) {
+  int64_t q = static_cast<int64_t>(static_cast<double>(a) / static_cast<double>(b));
+  if (q * b > a) --q;
+  else if ((q + 1) * b <= a) ++q;
+  return q;
+}
+// (W <= 65536 parts, P < 2^31 pages: every product below stays under 2^48)
+__device__ __forceinline__ int64_t part_start(int64_t w, int64_t P, int64_t W) { return div_floor53(w * P, W); }
 __device__ __forceinline__ int64_t part_of_page(int64_t x, int64_t P, int64_t W) {
-  return ((x + 1) * W - 1) / P;
+  return div_floor53((x + 1) * W - 1, P);
 }
 __device__ __forceinline__ int32_t pages_of(int32_t L, int32_t bs) { return (L + bs - 1) / bs; }
 

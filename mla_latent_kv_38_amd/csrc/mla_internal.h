@@ -81,6 +81,13 @@ hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t 
                              int32_t max_pages, int32_t bt_div, const int32_t* seq_lens,
                              const int32_t* seq_starts, float* ws_o, float* ws_lse, int64_t* ws_tbl, void* o_lat,
                              float* lse, hipStream_t s);
+// bf16 cache at 64-head multiples: each wave owns 32 heads and half of every
+// page (k_decode_h64w.hip).
+bool h64w_decode_supported(const mla_dims& d);
+hipError_t launch_decode_h64w(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
+                              const void* cache, const int32_t* block_table, int32_t max_pages, int32_t bt_div,
+                              const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o, float* ws_lse,
+                              int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s);
 hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
                               const void* q_abs, const void* cache, const float* kv_scale,
                               const int32_t* block_table, int32_t max_pages, int32_t bt_div,
