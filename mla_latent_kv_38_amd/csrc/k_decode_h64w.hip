@@ -135,10 +135,15 @@ struct PageDst {
 };
 
 __device__ __forceinline__ PageDst page_dst(const Lane& ln, const char* page, uint32_t buf_u) {
+  // the wave's row base is rederived at each call from an opaque copy of the
+  // wave index: kept alive instead, it ends up spilled across the page loop
+  int w = ln.wave;
+  asm volatile("" : "+s"(w));
+  const int r16 = (2 * (w >> 1) + (w & 1)) * 16;       // 32 th + 16 hb
   PageDst d;
-  d.src = uniform(page + (32 * ln.th + 16 * ln.hb) * kRowG);
-  d.lat = __builtin_amdgcn_readfirstlane(buf_u + (32 * ln.th + 16 * ln.hb) * kLatRow);
-  d.rope = __builtin_amdgcn_readfirstlane(buf_u + kLatB + (4 * ln.th + 2 * ln.hb) * kRopeBlk);
+  d.src = uniform(page + r16 * kRowG);
+  d.lat = __builtin_amdgcn_readfirstlane(buf_u + r16 * kLatRow);
+  d.rope = __builtin_amdgcn_readfirstlane(buf_u + kLatB + (r16 >> 3) * kRopeBlk);
   return d;
 }
 
@@ -374,6 +379,13 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(kCnt) : "memory");
 }
 
+// a wave-uniform 64-bit value into SGPRs
+__device__ __forceinline__ int64_t sgpr64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 __global__ void __launch_bounds__(256, 1) decode_h64w(
     int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2, const uint16_t* __restrict__ q_abs,
     const void* __restrict__ cache, const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
@@ -446,19 +458,18 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     const int64_t np = window_pages(Lb, st, kBs);
     const int64_t jp0 = x - first;
     const int64_t jp1 = min(np, jp0 + (x1 - x));
-    const int32_t* bt = block_table + (int64_t)(bt_div == 1 ? b : b / bt_div) * max_pages + fp;
-    if (jp0 == 0 && hg == 0 && threadIdx.x < 4) {                // the merge's part range of sequence b
-      const int64_t lp = part_of_page(first + np - 1, P, W);
-      const int t = threadIdx.x;
-      ws_tbl[4 * (int64_t)b + t] = t == 0 ? (int64_t)part : t == 1 ? lp : t == 2 ? np : P;
-    }
+    int32_t btd = bt_div;                                // opaque: no divider state kept across segments
+    asm volatile("" : "+s"(btd));
+    const int32_t* bt = block_table + (int64_t)(btd == 1 ? b : b / btd) * max_pages + fp;
 
     // This head group's 64 absorbed query rows (contiguous in q_abs, the same
     // 64 x 1152 B shape as a page) come into buffer 1 laid out like a page,
     // by the same 1 KiB direct loads; then the first page into buffer 0.  The
     // queries need no page id, so they go out first.
     {
-      const PageDst dq = page_dst(ln, reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg * 64) * kD),
+      int32_t hg_o = hg;                                 // opaque: the row address is not hoisted
+      asm volatile("" : "+s"(hg_o));
+      const PageDst dq = page_dst(ln, reinterpret_cast<const char*>(q_abs + ((int64_t)b * n_h + (int64_t)hg_o * 64) * kD),
                                   uniform_lds((LDSP char*)g_buf1));
       static_for<18>([&](auto I) { issue_load<I>(ln, dq); });
     }
@@ -467,6 +478,15 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     {
       const PageDst d0 = page_dst(ln, cbase + (int64_t)pg0 * kPageG, uniform_lds((LDSP char*)g_buf0));
       static_for<18>([&](auto I) { issue_load<I>(ln, d0); });
+    }
+    if (jp0 == 0 && hg == 0 && threadIdx.x < 4) {                // the merge's part range of sequence b
+      // (written once the loads are out: its operands may come from scratch)
+      int64_t Po = sgpr64(P);                            // opaque, as above
+      int t = threadIdx.x;
+      asm volatile("" : "+s"(Po));
+      asm volatile("" : "+v"(t));
+      const int64_t lp = part_of_page(first + np - 1, Po, W);
+      ws_tbl[4 * (int64_t)b + t] = t == 0 ? (int64_t)part : t == 1 ? lp : t == 2 ? np : Po;
     }
     Acc acc;
 #pragma unroll
@@ -482,12 +502,14 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     bf16x8 qf[36];
     {
       const LDSP char* qb = (const LDSP char*)g_buf1;
-      const int h = 32 * ln.hb + ln.l32;
-      const uint32_t q_lat = h * kLatRow + 16 * ln.hi;
+      int lq = ln.lane;                                  // opaque: these addresses are not hoisted
+      asm volatile("" : "+v"(lq));
+      const int h = 32 * ln.hb + (lq & 31);
+      const uint32_t q_lat = h * kLatRow + 16 * (lq >> 5);
       const int blk = h >> 3, t8 = h & 7;
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) {
-        const uint32_t off = kb < 32 ? q_lat + 32 * kb : kLatB + blk * kRopeBlk + 128 * t8 + 16 * ((2 * (kb - 32) + ln.hi) ^ t8);
+        const uint32_t off = kb < 32 ? q_lat + 32 * kb : kLatB + blk * kRopeBlk + 128 * t8 + 16 * ((2 * (kb - 32) + (lq >> 5)) ^ t8);
         qf[kb] = *(const LDSP bf16x8*)(qb + off);
       }
 #pragma unroll
@@ -523,8 +545,11 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     // dozens of them alive (and spilled) across the whole segment loop.
     Lane le = ln;
     asm volatile("" : "+v"(le.lane));
+    asm volatile("" : "+s"(le.wave));
     le.l32 = le.lane & 31;
     le.hi = le.lane >> 5;
+    le.hb = le.wave & 1;
+    le.th = le.wave >> 1;
     const float l_half = sum_xor32(acc.l_own);
     if (le.hi == 0) {
       g_xm[le.th * 64 + le.hb * 32 + le.l32] = acc.m_ref;
@@ -597,7 +622,25 @@ __global__ void __launch_bounds__(256) combine_h64w(int32_t B, int32_t n_h, int3
   const int col = 32 * (8 * th + cl) + 16 * qq + 4 * hi;
   const int hh = 32 * hb + l32;                       // head within the group
   const int64_t head = (int64_t)b * n_h + (int64_t)hg * 64 + hh;
-  const int64_t np = window_pages(seq_lens[b], seq_start(seq_starts, b), kBs);
+  // the part range is loaded together with the length (it is only stale for
+  // an empty sequence, which no part covers and which does not read it)
+  u32x4 wr;
+  u32x2 pr;
+  int32_t len;
+  asm volatile("s_load_dwordx4 %0, %3, 0x0\n\t"
+               "s_load_dwordx2 %1, %3, 0x18\n\t"
+               "s_load_dword %2, %4, 0x0\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&s"(wr), "=&s"(pr), "=&s"(len)
+               : "s"(ws_tbl + 4 * (int64_t)b), "s"(seq_lens + b)
+               : "memory");
+  const int64_t w0 = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(wr[1])) << 32) |
+                                          static_cast<uint32_t>(wr[0]));
+  const int64_t w1 = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(wr[3])) << 32) |
+                                          static_cast<uint32_t>(wr[2]));
+  const int64_t P = static_cast<int64_t>((static_cast<uint64_t>(static_cast<uint32_t>(pr[1])) << 32) |
+                                         static_cast<uint32_t>(pr[0]));
+  const int64_t np = window_pages(len, seq_start(seq_starts, b), kBs);
   if (np == 0) {                                      // empty sequence: zero output, lse = -inf
     *reinterpret_cast<u32x2*>(o_lat + head * kDc + col) = u32x2{0u, 0u};
     *reinterpret_cast<u32x2*>(o_lat + head * kDc + col + 8) = u32x2{0u, 0u};
@@ -607,8 +650,6 @@ __global__ void __launch_bounds__(256) combine_h64w(int32_t B, int32_t n_h, int3
     }
     return;
   }
-  const int64_t w0 = ws_tbl[4 * (int64_t)b], w1 = ws_tbl[4 * (int64_t)b + 1];
-  const int64_t P = ws_tbl[4 * (int64_t)b + 3];
   if (w0 == w1) return;                               // one part: written by the decode kernel
   const bool all_live = P >= W;
   const uint16_t* ws16 = reinterpret_cast<const uint16_t*>(ws_o);
