@@ -53,7 +53,8 @@ def parse():
 # Kernel sources the stored HBM-traffic measurement depends on; the stored
 # figure is reported only while their hash matches.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-TRAFFIC_SOURCES = ["mla_latent_kv_38_amd/csrc/k_decode_mfma.hip", "mla_latent_kv_38_amd/csrc/mla_device.h"]
+TRAFFIC_SOURCES = ["mla_latent_kv_38_amd/csrc/k_decode_h64w.hip", "mla_latent_kv_38_amd/csrc/k_decode_mfma.hip",
+                   "mla_latent_kv_38_amd/csrc/k_decode_fp8.hip", "mla_latent_kv_38_amd/csrc/mla_device.h"]
 
 
 def source_hash(paths):
@@ -97,6 +98,9 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n, "copies": 3}))
 
 
+EXTRA_WORKLOADS = ("ragged_b64", "long_b4_128k", "fp8_h16_b128")
+
+
 def main():
     args = parse()
     if args.copy_probe:
@@ -112,7 +116,81 @@ def main():
     import mla_latent_kv_38_amd as mla
 
     dev = torch.device("cuda:0")
-    w = W.make(args.workload)
+    peaks = achievable_peaks(mla, dev)
+    res, w, row_bytes = measure(args, W, mla, dev, args.workload, args.steps, args.warmup, extras=not args.no_extras)
+    _against_achievable(res["roofline"], peaks)
+    res["achievable_peaks"] = peaks
+    if not args.no_extras and args.workload == "v2_b16_4k":
+        # the other workloads, decode-step lines of their own (fewer steps)
+        res["workloads"] = {}
+        for name in EXTRA_WORKLOADS:
+            r, _, _ = measure(args, W, mla, dev, name, min(args.steps, 30), min(args.warmup, 5), extras=False)
+            _against_achievable(r["roofline"], peaks)
+            res["workloads"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "decode_us", "call_us",
+                                                         "roofline", "config")}
+            torch.cuda.empty_cache()
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_s, row_bytes)
+    print(json.dumps(res))
+
+
+def _against_achievable(roof, peaks):
+    """The decode's rate as a fraction of what the probes achieved too."""
+    a = peaks["hbm_read_GBps"] if roof["bound"] == "hbm" else peaks["bf16_mfma_TFLOPs"]
+    roof["achievable_peak"] = a
+    roof["frac_of_achievable"] = round(roof["achieved"] / a, 4)
+
+
+def achievable_peaks(mla, dev, read_gib=2, mfma_iters=2000, mfma_wgs=2048, reps=5):
+    """What the chip achieves on a plain streaming read of read_gib GiB (one
+    pass, 2048 workgroups, 16-B nontemporal loads) and on a plain bf16 MFMA
+    loop (mfma_wgs workgroups of 4 waves, four independent 32x32x16 chains
+    each), timed with events on the launch stream, best of `reps`."""
+    import ctypes
+
+    import torch
+    lib = mla._lib.lib()
+    stream = torch.cuda.current_stream()
+    n = read_gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.zeros(max(8192, 4 * mfma_wgs), dtype=torch.uint8, device=dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best(launch):
+        launch()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            launch()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return min(ts)
+
+    def rd():
+        mla._lib.check(lib.mla_probe_stream_read(ctypes.c_void_p(buf.data_ptr()), n, ctypes.c_void_p(sink.data_ptr()),
+                                                 sp), "mla_probe_stream_read")
+
+    def mm():
+        mla._lib.check(lib.mla_probe_mfma_bf16(mfma_iters, mfma_wgs, ctypes.c_void_p(sink.data_ptr()), sp),
+                       "mla_probe_mfma_bf16")
+    t_rd = best(rd)
+    t_mm = best(mm)
+    flops = 16.0 * 32768 * mfma_iters * mfma_wgs
+    del buf
+    torch.cuda.empty_cache()
+    return {"hbm_read_GBps": round(n / t_rd / 1e9, 1), "read_bytes": n,
+            "bf16_mfma_TFLOPs": round(flops / t_mm / 1e12, 1), "mfma_flops": flops,
+            "spec": {"hbm_GBps": HBM_PEAK_GBPS, "bf16_mfma_TFLOPs": BF16_PEAK_TFLOPS}}
+
+
+def measure(args, W, mla, dev, name, steps, warmup, extras):
+    """One workload's decode steps; returns (result line fields, workload,
+    cache row bytes)."""
+    import torch
+    w = W.make(name)
     B, nh, D = w.B, w.n_h, w.D
     act = torch.bfloat16 if w.act == "bf16" else torch.float32
     d = mla.make_dims(w.n_h, w.d_h, w.d_c, w.d_R, w.block_size, act=w.act, kv=w.kv,
@@ -182,7 +260,7 @@ def main():
         mla.up_v(d, o_lat, rp["w_uv"], out)
         rec(4)
 
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     graphs = None
@@ -195,7 +273,7 @@ def main():
             with torch.cuda.graph(gph):
                 step(r)
             graphs.append(gph)
-        for i in range(args.warmup):
+        for i in range(warmup):
             graphs[i % R].replay()
         torch.cuda.synchronize()
 
@@ -203,10 +281,10 @@ def main():
     # roofline kernel), on the stream the library launches on
     new_ev = lambda: torch.cuda.Event(enable_timing=True)
     t0, t1 = new_ev(), new_ev()
-    dec_evs = [[None, None, new_ev(), new_ev(), None] for _ in range(args.steps)]
+    dec_evs = [[None, None, new_ev(), new_ev(), None] for _ in range(steps)]
     torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         if graphs is not None:
             graphs[i % R].replay()
         else:
@@ -214,12 +292,12 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
+    ms_step = ms_total / steps
     dec_us = None if graphs is not None else float(np.mean([e[2].elapsed_time(e[3]) for e in dec_evs]) * 1e3)
 
     # per-call breakdown: a second, untimed pass with an event between calls
-    evs = [[new_ev() for _ in range(5)] for _ in range(args.steps)]
-    for i in range(args.steps):
+    evs = [[new_ev() for _ in range(5)] for _ in range(steps)]
+    for i in range(steps):
         step(i, evs[i])
     torch.cuda.synchronize()
     call_us = {name: float(np.mean([e[k].elapsed_time(e[k + 1]) for e in evs]) * 1e3)
@@ -228,7 +306,7 @@ def main():
         dec_us = call_us["decode"]
 
     kvp = mq = e8 = None
-    if not args.no_extras:
+    if extras:
         kvp = kv_project_measure(mla, d, w, dev, B, args.min_replica_mb)
         mq = multi_query_measure(mla, d, w, dev, reps, bt, lens, act, iters=20)
         if w.kv == "bf16" and w.act == "bf16" and w.n_h % 64 == 0:
@@ -252,7 +330,7 @@ def main():
     else:
         roof = dict(bound="mfma", achieved=round(ach_tflops, 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                     frac=round(ach_tflops / BF16_PEAK_TFLOPS, 4))
-    roof.update(traffic=stored_traffic(args.workload), kernel="mla_decode (split + combine)",
+    roof.update(traffic=stored_traffic(name), kernel="mla_decode (split + combine)",
                 algorithmic_bytes=dec_bytes,
                 algorithmic_flops=dec_flops, avg_us=round(dec_us, 3),
                 tflops=round(ach_tflops, 1), tflops_frac=round(ach_tflops / BF16_PEAK_TFLOPS, 4))
@@ -261,10 +339,10 @@ def main():
 
     res = {
         "metric": METRIC, "value": round(step_kv_gbps, 1), "unit": "GB/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "steps": steps, "warmup": warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.act,
         "data": "synthetic",
-        "config": {"workload": args.workload, "batch": B, "seq_len": int(w.lens.max()),
+        "config": {"workload": name, "batch": B, "seq_len": int(w.lens.max()),
                    "total_tokens": toks, "n_heads": nh, "d_head": w.d_h, "d_latent": w.d_c,
                    "d_rope": w.d_R, "block_size": w.block_size, "kv_dtype": w.kv,
                    "replicas": R, "num_splits": args.splits,
@@ -280,9 +358,8 @@ def main():
         "e4m3_cache": e8,
     }
 
-    if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_s, row_bytes)
-    print(json.dumps(res))
+    del reps, ws
+    return res, w, row_bytes
 
 
 def kv_project_measure(mla, d, w, dev, T, min_mb, d_model=5120, iters=50):

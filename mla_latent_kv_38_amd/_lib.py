@@ -25,6 +25,8 @@ SIGNATURES = {
     "mla_kv_project_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32]),
     "mla_kv_project_append": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
                                         c_void_p, c_int64, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
+    "mla_probe_stream_read": (c_int32, [c_void_p, c_size_t, c_void_p, c_void_p]),
+    "mla_probe_mfma_bf16": (c_int32, [c_int32, c_int32, c_void_p, c_void_p]),
     "mla_decode_workspace_bytes": (c_size_t, [c_void_p, c_int32, c_int32]),
     "mla_decode": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_void_p,
                              c_int32, c_void_p, c_size_t, c_void_p, c_void_p, c_void_p]),

@@ -13,7 +13,7 @@ LIB_NAME = "libmla_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = ["mla_api.hip", "k_generic.hip", "k_decode_mfma.hip", "k_decode_fp8.hip", "k_proj_mfma.hip",
            "k_kvproj.hip",
-           "k_decode_h64w.hip"]
+           "k_decode_h64w.hip", "probes.hip"]
 
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 # Packed-fp32 VALU forms are disabled for every device pass.

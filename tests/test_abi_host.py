@@ -19,9 +19,10 @@ def _lib():
 
 
 def _header_functions():
-    src = open(os.path.join(ROOT, "include", "mla.h")).read()
+    inc = os.path.join(ROOT, "include")
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(mla_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -147,3 +148,15 @@ def test_workspace_grows_with_splits_and_batch():
     assert a < b < c
     # one float32 partial (d_latent values + lse) per head per slot, slots = splits + batch
     assert b >= (64 + 16) * 128 * (512 + 1) * 4
+
+
+def test_probes_reject_bad_arguments_before_launching():
+    lib = _lib()
+    assert lib.mla_probe_stream_read(NULL, 1024, FAKE, NULL) == -1
+    assert lib.mla_probe_stream_read(FAKE, 1024, NULL, NULL) == -1
+    assert lib.mla_probe_stream_read(FAKE, 0, FAKE, NULL) == -2
+    assert lib.mla_probe_stream_read(FAKE, 1000, FAKE, NULL) == -2
+    assert lib.mla_probe_stream_read(ctypes.c_void_p(0x1008), 1024, FAKE, NULL) == -2
+    assert lib.mla_probe_mfma_bf16(100, 256, NULL, NULL) == -1
+    assert lib.mla_probe_mfma_bf16(0, 256, FAKE, NULL) == -2
+    assert lib.mla_probe_mfma_bf16(100, 0, FAKE, NULL) == -2
