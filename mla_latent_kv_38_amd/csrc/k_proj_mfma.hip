@@ -83,7 +83,18 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t bpw, int
     else append_row_576<false>(c, kp, app.pos[t], app.slot[t], app.cache, app.kv_scale, log2_base, ln);
     return;
   }
-  const int h = blockIdx.x / cblocks, cb = blockIdx.x % cblocks;
+  // Workgroup i runs on XCD i % 8.  When the head count is a multiple of 8,
+  // the column blocks of a head go to one XCD, so its q_C rows are fetched
+  // from HBM once (their L2 is shared).
+  int h, cb;
+  if ((n_h & 7) == 0) {
+    const int j = blockIdx.x >> 3;
+    h = (j / cblocks) * 8 + (blockIdx.x & 7);
+    cb = j % cblocks;
+  } else {
+    h = blockIdx.x / cblocks;
+    cb = blockIdx.x % cblocks;
+  }
   const int c0 = cb * kAbsCols;
   const int b_lo = blockIdx.y * bpw, b_hi = min(B, b_lo + bpw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -211,7 +222,17 @@ __global__ void __launch_bounds__(256) up_v_mfma(int32_t B, int32_t bpw, int32_t
   constexpr int kRowB = d_c * 2 + 16;
   __shared__ __attribute__((aligned(16))) char otile[2][16 * kRowB];   // double-buffered batch blocks
   const int iblocks = d_h / 64;
-  const int h = blockIdx.x / iblocks, ib = blockIdx.x % iblocks;
+  // the feature blocks of a head on one XCD (as in absorb_q): its o_lat rows
+  // come from HBM once
+  int h, ib;
+  if ((n_h & 7) == 0) {
+    const int j = blockIdx.x >> 3;
+    h = (j / iblocks) * 8 + (blockIdx.x & 7);
+    ib = j % iblocks;
+  } else {
+    h = blockIdx.x / iblocks;
+    ib = blockIdx.x % iblocks;
+  }
   const int b_lo = blockIdx.y * bpw, b_hi = min(B, b_lo + bpw);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, s = lane & 15;
@@ -292,7 +313,9 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, c
   int nsplit = std::max((nblocks + kMaxBlk - 1) / kMaxBlk, std::min(nblocks, (256 + wgs - 1) / wgs));
   const int bpw = 16 * ((nblocks + nsplit - 1) / nsplit);
   nsplit = (B + bpw - 1) / bpw;
-  const dim3 grid(wgs + (app.T + 3) / 4, nsplit);
+  // (append workgroups padded to a multiple of 8, so that workgroup x of every
+  // grid row runs on XCD x % 8; the extra ones have no row and return)
+  const dim3 grid(wgs + (((app.T + 3) / 4 + 7) & ~7), nsplit);
   auto qc = static_cast<const uint16_t*>(q_c);
   auto qr = static_cast<const uint16_t*>(q_r);
   auto w = static_cast<const uint16_t*>(w_uk);

@@ -68,3 +68,28 @@ def test_full_size_sampled(name):
             assert np.array_equal(g[:, :w.d_c], e[:, :w.d_c]), f"latent b={b}"
             ulp = np.abs(g[:, w.d_c:] - e[:, w.d_c:]) / np.maximum(np.abs(e[:, w.d_c:]), 1e-30)
             assert (ulp <= 2.0 ** -8).all(), f"rope b={b}"
+
+
+@pytest.mark.parametrize("name", ["v2_b16_4k", "v2_b16_4k_e4m3"])
+def test_split_partials_stay_near_the_unsplit_result(name):
+    """The split path stores each part's normalised partial as bfloat16 before
+    the merge: one rounding more than a sequence decoded in one piece.  One
+    bf16 rounding moves an element by at most 2^-9 of itself, and a partial is
+    a convex combination of the same latent rows as the whole result, so the
+    merged output must stay within a small multiple of 2^-9 max|o_lat| of the
+    unsplit one; this bounds it by 4e-3 max|o_lat| (the output tolerance is
+    1e-2), and lse (float32 on both paths) within 1e-5."""
+    w = W.make(name)
+    res = C.run_chain(w)                       # automatic split: partials for every sequence
+    d = C.dims_of(w)
+    bt = C.to_dev(w.block_table, torch.int32)
+    sl = C.to_dev(w.lens, torch.int32)
+    import mla_latent_kv_38_amd as mla
+    whole_o, whole_l = mla.decode(d, res["q_abs"], res["cache"], bt, sl, kv_scale=res["scale"], num_splits=1)
+    torch.cuda.synchronize()
+    a, b = C.f64(res["o_lat"]), C.f64(whole_o)
+    err = np.abs(a - b).max() / np.abs(b).max()
+    print(f"[split vs whole] {name}: max|diff|/max|o| = {err:.3e}", flush=True)
+    assert err <= 4e-3
+    la, lb = C.f64(res["lse"]), C.f64(whole_l)
+    assert np.abs(la - lb).max() <= 1e-5 * max(1.0, np.abs(lb).max())
