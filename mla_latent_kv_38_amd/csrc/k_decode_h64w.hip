@@ -82,6 +82,35 @@ struct Lane {
   uint32_t v_lat, v_rope;  // direct loads: per-lane source offsets
 };
 
+// ---- optional cycle stamps -------------------------------------------------
+// Built with -DMLA_CYCLE_STAMPS (mla_latent_kv_38_amd/cycle_stamps.py does so
+// into a separate library), the kernel accumulates s_memtime stamps around
+// its phases and wave 0 of each workgroup writes them to mla_stamp_buf;
+// without it every macro below is empty and the code is unchanged.
+#ifdef MLA_CYCLE_STAMPS
+struct Stamps {
+  unsigned long long wait = 0, bar = 0, qk = 0, sm = 0, pv = 0, pages = 0, ep = 0;
+  unsigned long long t_start = 0, rt_start = 0, t_locate = 0, t_qissue = 0, t_loop = 0;
+};
+#define ST_NOW(v) const unsigned long long v = __builtin_amdgcn_s_memtime()
+#define ST_ADD(o, f, a, b) ((o).f += (b) - (a))
+#define ST_SET(o, f, v) ((o).f = (v))
+#define ST_SET_ONCE(o, f, v) ((o).f = (o).f ? (o).f : (v))
+#define ST_ARG , Stamps& stm
+#define ST_PASS , stm
+constexpr int kStampFields = 14;
+constexpr int kStampGroups = 4096;
+__device__ unsigned long long mla_stamp_buf[kStampGroups * kStampFields];
+#else
+struct Stamps {};
+#define ST_NOW(v)
+#define ST_ADD(o, f, a, b)
+#define ST_SET(o, f, v)
+#define ST_SET_ONCE(o, f, v)
+#define ST_ARG
+#define ST_PASS
+#endif
+
 // Token (row of the page) that MFMA row m of token half th stands for.  With
 // m = 16u + 8e + 4h + a this is 32 th + 16u + 4a + 2e + h: the QK output
 // register r = 8u + 4e + a of lane half h is then the score of row
@@ -267,10 +296,13 @@ __device__ __forceinline__ f32x16 qk_page(const Lane& ln, const LDSP char* __res
 // about the same time; the L2 serves the second request from the first fill.)
 __device__ __forceinline__ void page_step(const Lane& ln, const LDSP char* __restrict__ buf, bool fresh,
                                           const PageDst& nd, const bf16x8 (&qf)[36], int nvalid, int lo, float s2,
-                                          Acc& acc) {
+                                          Acc& acc ST_ARG) {
 
   // ---- QK ----------------------------------------------------------------
+  ST_NOW(t0);
   f32x16 S = qk_page<true>(ln, buf, nd, qf);
+  ST_NOW(t1);
+  ST_ADD(stm, qk, t0, t1);
 
   // ---- softmax (inside the wave) -----------------------------------------
   const bool partial = nvalid < kBs || lo > 0;
@@ -318,8 +350,15 @@ __device__ __forceinline__ void page_step(const Lane& ln, const LDSP char* __res
                                              pack2_bf16(S[8 * u + 6], S[8 * u + 7])});
 
   // ---- PV: 16 column blocks x 2 k-steps ----------------------------------
+  ST_NOW(t2);
+  ST_ADD(stm, sm, t1, t2);
   if (partial) pv_page<true, false>(ln, buf, nd, pb, nvalid, lo, acc);
   else pv_page<false, false>(ln, buf, nd, pb, nvalid, lo, acc);
+#ifdef MLA_CYCLE_STAMPS
+  MFMA_RESULT_WAIT();                                  // (the products' time, not just their issue)
+#endif
+  ST_NOW(t3);
+  ST_ADD(stm, pv, t2, t3);
 }
 
 // Segment epilogue helpers (the token half TH is a template argument so that
@@ -392,6 +431,11 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     const int32_t* __restrict__ seq_lens, const int32_t* __restrict__ seq_starts, float* __restrict__ ws_o,
     float* __restrict__ ws_lse, int64_t* __restrict__ ws_tbl, uint16_t* __restrict__ o_lat,
     float* __restrict__ lse) {
+#ifdef MLA_CYCLE_STAMPS
+  Stamps stm;
+  stm.t_start = __builtin_amdgcn_s_memtime();
+  stm.rt_start = __builtin_amdgcn_s_memrealtime();
+#endif
   Lane ln;
   const int tid = threadIdx.x;
   ln.lane = tid & 63;
@@ -425,6 +469,8 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
   }
 
   const PartRange pr = locate_part(seq_lens, seq_starts, B, kBs, part, W, g_lens);
+  ST_NOW(t_loc);
+  ST_SET(stm, t_locate, t_loc);
   if (pr.x0 >= pr.x1) return;
   const bool lens_in_lds = pr.chunk == 1;
   const int64_t P = pr.P;
@@ -473,6 +519,8 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
                                   uniform_lds((LDSP char*)g_buf1));
       static_for<18>([&](auto I) { issue_load<I>(ln, dq); });
     }
+    ST_NOW(t_qi);
+    ST_SET_ONCE(stm, t_qissue, t_qi);
     int32_t pg0, pg_next;                                // ids of the first two pages, one round trip
     sload2_i32(bt + jp0, bt + (jp0 + 1 < jp1 ? jp0 + 1 : jp0), &pg0, &pg_next);
     {
@@ -517,6 +565,8 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     }
     __syncthreads();                                     // buffer 1 free for the second page
 
+    ST_NOW(t_lp);
+    ST_SET_ONCE(stm, t_loop, t_lp);
     const int32_t j0 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(jp0));
     const int32_t j1 = __builtin_amdgcn_readfirstlane(static_cast<int32_t>(jp1));
     const int32_t Lu = __builtin_amdgcn_readfirstlane(L);
@@ -525,19 +575,26 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
       const bool even = ((jp - j0) & 1) == 0;
       const LDSP char* buf = even ? (const LDSP char*)g_buf0 : (const LDSP char*)g_buf1;
       const uint32_t nbuf_u = uniform_lds(even ? (LDSP char*)g_buf1 : (LDSP char*)g_buf0);
+      ST_NOW(tw0);
       wait_vm<0>();                                      // this wave's loads of page jp (and the queries)
+      ST_NOW(tw1);
       __syncthreads();                                   // every wave's loads landed; page jp-1 consumed
+      ST_NOW(tw2);
+      ST_ADD(stm, wait, tw0, tw1);
+      ST_ADD(stm, bar, tw1, tw2);
+      ST_ADD(stm, pages, 0, 1);
       const bool more = jp + 1 < j1;
       const PageDst nd = page_dst(ln, more ? cbase + (int64_t)pg_next * kPageG : qrows, nbuf_u);
       // id two ahead, read during this page (constant address space: a scalar load)
       const int32_t pg2 = jp + 2 < j1 ? ((const __attribute__((address_space(4))) int32_t*)bt)[jp + 2] : 0;
       const int nvalid = min(kBs, Lu - jp * kBs);
       const int plo = jp == 0 ? lo : 0;
-      page_step(ln, buf, jp == j0, nd, qf, nvalid, plo, s2, acc);
+      page_step(ln, buf, jp == j0, nd, qf, nvalid, plo, s2, acc ST_PASS);
       pg_next = pg2;
     }
     wait_vm<0>();                                        // the last page's loads (query rows) landed
 
+    ST_NOW(te0);
     // ---- segment epilogue: merge the token halves, normalise, store ---------
     MFMA_RESULT_WAIT();                                  // last products' results
     // The epilogue's per-lane addresses are derived from an opaque copy of the
@@ -582,6 +639,8 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     if (le.th == 0) take_and_store<0>(acc, sc, sc_p, xch, ln, whole, dst);
     else take_and_store<1>(acc, sc, sc_p, xch, ln, whole, dst);
 
+    ST_NOW(te1);
+    ST_ADD(stm, ep, te0, te1);
     const int64_t xn = x + (jp1 - jp0);
     if (xn >= x1) break;
     int32_t bn = b;
@@ -595,6 +654,17 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     }
     __syncthreads();
   }
+#ifdef MLA_CYCLE_STAMPS
+  if (tid == 0 && blockIdx.x < kStampGroups) {
+    unsigned long long* o = mla_stamp_buf + (int64_t)blockIdx.x * kStampFields;
+    const unsigned long long t_end = __builtin_amdgcn_s_memtime(), rt_end = __builtin_amdgcn_s_memrealtime();
+    const unsigned long long v[kStampFields] = {t_end - stm.t_start, stm.t_locate - stm.t_start,
+                                                stm.t_qissue - stm.t_start, stm.t_loop - stm.t_start, stm.wait,
+                                                stm.bar, stm.qk, stm.sm, stm.pv, stm.pages, stm.ep, stm.rt_start,
+                                                rt_end, 1};
+    for (int i = 0; i < kStampFields; ++i) o[i] = v[i];
+  }
+#endif
 }
 
 // ---------------------------------------------------------------------------
@@ -720,5 +790,13 @@ hipError_t launch_decode_h64w(const mla_dims& d, const DecodePlan& plan, int32_t
                                            static_cast<uint16_t*>(o_lat), lse);
   return hipGetLastError();
 }
+
+#ifdef MLA_CYCLE_STAMPS
+// Readers of the stamps (only in the stamped build).
+extern "C" int mla_stamps_read(void* host, size_t bytes) {
+  return static_cast<int>(hipMemcpyFromSymbol(host, HIP_SYMBOL(mla_stamp_buf), bytes, 0, hipMemcpyDeviceToHost));
+}
+extern "C" int mla_stamps_fields() { return kStampFields; }
+#endif
 
 }  // namespace mla

@@ -73,12 +73,16 @@ def test_full_size_sampled(name):
 @pytest.mark.parametrize("name", ["v2_b16_4k", "v2_b16_4k_e4m3"])
 def test_split_partials_stay_near_the_unsplit_result(name):
     """The split path stores each part's normalised partial as bfloat16 before
-    the merge: one rounding more than a sequence decoded in one piece.  One
-    bf16 rounding moves an element by at most 2^-9 of itself, and a partial is
-    a convex combination of the same latent rows as the whole result, so the
-    merged output must stay within a small multiple of 2^-9 max|o_lat| of the
-    unsplit one; this bounds it by 4e-3 max|o_lat| (the output tolerance is
-    1e-2), and lse (float32 on both paths) within 1e-5."""
+    the merge: one rounding more than a sequence decoded in one piece
+    (num_splits = 1 puts every sequence in one piece here).  That rounding
+    moves a partial's element by at most 2^-9 of its magnitude, and the
+    partials are convex combinations of the same latent rows as the result,
+    so before the final rounding the two results differ by about 2^-9
+    max|o_lat|; after it, each element may also land one bf16 unit in the
+    last place apart.  Bound: |split - unsplit| <= ulp(unsplit) + 2^-9
+    max|o_lat| element by element (for the large elements about 3x tighter
+    than the 1e-2 output tolerance), and lse (float32 on both paths) within
+    1e-5."""
     w = W.make(name)
     res = C.run_chain(w)                       # automatic split: partials for every sequence
     d = C.dims_of(w)
@@ -88,8 +92,12 @@ def test_split_partials_stay_near_the_unsplit_result(name):
     whole_o, whole_l = mla.decode(d, res["q_abs"], res["cache"], bt, sl, kv_scale=res["scale"], num_splits=1)
     torch.cuda.synchronize()
     a, b = C.f64(res["o_lat"]), C.f64(whole_o)
-    err = np.abs(a - b).max() / np.abs(b).max()
-    print(f"[split vs whole] {name}: max|diff|/max|o| = {err:.3e}", flush=True)
-    assert err <= 4e-3
+    mag = np.maximum(np.abs(b), np.finfo(np.float32).tiny)
+    ulp = np.exp2(np.floor(np.log2(mag)) - 7)
+    diff = np.abs(a - b)
+    bound = ulp + 2.0 ** -9 * np.abs(b).max()
+    print(f"[split vs whole] {name}: max|diff|/max|o| = {diff.max() / np.abs(b).max():.3e}, "
+          f"differing {np.mean(diff > 0):.3%}, worst diff/bound {np.max(diff / bound):.3f}", flush=True)
+    assert np.all(diff <= bound)
     la, lb = C.f64(res["lse"]), C.f64(whole_l)
     assert np.abs(la - lb).max() <= 1e-5 * max(1.0, np.abs(lb).max())
