@@ -328,12 +328,12 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
         *reinterpret_cast<u32x2*>(o_lat + ((int64_t)b * n_h + head) * kDc + col) =
             u32x2{pack2_bf16(o[0], o[1]), pack2_bf16(o[2], o[3])};
       else
-        *reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + head) * kDc + col) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<f32x4*>(ws_o + (((int64_t)part + b) * n_h + head) * kDc + col));
     }
     if (wave == 0 && g == 0) {
       const float lse_v = (M + __log2f(Lsum)) * 0.69314718055994531f;
       if (whole) { if (lse) lse[(int64_t)b * n_h + head] = lse_v; }
-      else ws_lse[((int64_t)part + b) * n_h + head] = lse_v;
+      else __builtin_nontemporal_store(lse_v, ws_lse + ((int64_t)part + b) * n_h + head);
     }
 
     x += jp1 - jp0;

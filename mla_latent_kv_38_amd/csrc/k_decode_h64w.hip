@@ -406,9 +406,10 @@ __device__ __forceinline__ void take_and_store(const Acc& acc, float sc, float s
     } else {
 #pragma unroll
       for (int qq = 0; qq < 2; ++qq)
-        *reinterpret_cast<u32x4*>(dst + ((((ln.hb * 2 + TH) * 8 + c) * 2 + qq) * 64 + ln.lane) * 8) =
+        __builtin_nontemporal_store(
             u32x4{pack2_bf16(v[8 * qq], v[8 * qq + 1]), pack2_bf16(v[8 * qq + 2], v[8 * qq + 3]),
-                  pack2_bf16(v[8 * qq + 4], v[8 * qq + 5]), pack2_bf16(v[8 * qq + 6], v[8 * qq + 7])};
+                  pack2_bf16(v[8 * qq + 4], v[8 * qq + 5]), pack2_bf16(v[8 * qq + 6], v[8 * qq + 7])},
+            reinterpret_cast<u32x4*>(dst + ((((ln.hb * 2 + TH) * 8 + c) * 2 + qq) * 64 + ln.lane) * 8));
     }
   }
 }
@@ -632,7 +633,7 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
     if (le.th == 0 && le.hi == 0) {
       const float lse_v = (M + __log2f(lt)) * 0.69314718055994531f;
       if (whole) { if (lse) lse[(int64_t)b * n_h + head] = lse_v; }
-      else ws_lse[((int64_t)part + b) * n_h + head] = lse_v;
+      else __builtin_nontemporal_store(lse_v, ws_lse + ((int64_t)part + b) * n_h + head);
     }
     uint16_t* dst = whole ? o_lat + ((int64_t)b * n_h + head) * kDc
                           : reinterpret_cast<uint16_t*>(ws_o) + (((int64_t)part + b) * n_h + (int64_t)hg * 64) * kDc;
@@ -734,7 +735,7 @@ __global__ void __launch_bounds__(256) combine_h64w(int32_t B, int32_t n_h, int3
       const int64_t w = base + jj;
       const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
       const int64_t slot = (live ? w : w0) + b;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(ws16 + slot * n_h * kDc + off);
+      const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ws16 + slot * n_h * kDc + off));
       v0[jj] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
                      __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
       v1[jj] = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),

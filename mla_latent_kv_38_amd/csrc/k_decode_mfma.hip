@@ -585,7 +585,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       const int64_t head = (int64_t)hg * 64 + hh;
       if (ln.wave == 0 && ln.hi == 0) {
         if (whole) { if (lse) lse[(int64_t)b * n_h + head] = lse_v; }
-        else ws_lse[((int64_t)part + b) * n_h + head] = lse_v;
+        else __builtin_nontemporal_store(lse_v, ws_lse + ((int64_t)part + b) * n_h + head);
       }
     }
     if (whole) {
@@ -610,11 +610,11 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
         for (int q4 = 0; q4 < 4; ++q4) {
           const f32x16& o0 = acc.o[cb][0];
           const f32x16& o1 = acc.o[cb][1];
-          *reinterpret_cast<u32x4*>(wp + ((ln.wave * 4 + cb) * 4 + q4) * 512) =
-              u32x4{pack2_bf16(o0[4 * q4] * inv[0], o0[4 * q4 + 1] * inv[0]),
-                    pack2_bf16(o0[4 * q4 + 2] * inv[0], o0[4 * q4 + 3] * inv[0]),
-                    pack2_bf16(o1[4 * q4] * inv[1], o1[4 * q4 + 1] * inv[1]),
-                    pack2_bf16(o1[4 * q4 + 2] * inv[1], o1[4 * q4 + 3] * inv[1])};
+          __builtin_nontemporal_store(u32x4{pack2_bf16(o0[4 * q4] * inv[0], o0[4 * q4 + 1] * inv[0]),
+                                            pack2_bf16(o0[4 * q4 + 2] * inv[0], o0[4 * q4 + 3] * inv[0]),
+                                            pack2_bf16(o1[4 * q4] * inv[1], o1[4 * q4 + 1] * inv[1]),
+                                            pack2_bf16(o1[4 * q4 + 2] * inv[1], o1[4 * q4 + 3] * inv[1])},
+                                      reinterpret_cast<u32x4*>(wp + ((ln.wave * 4 + cb) * 4 + q4) * 512));
         }
     }
 
