@@ -40,8 +40,11 @@
  *     HIP include; the caller casts.
  *   - Decode calls take no maximum-length hint: the split-KV plan (how many
  *     chunks, how much workspace) depends only on the batch size, the head
- *     count and num_splits, and the kernels read the lengths themselves, so
- *     the same workspace serves any lengths within the block table.
+ *     count, num_splits and the current device's compute-unit count (asked
+ *     of the runtime once per device; 256 when no device answers), and the
+ *     kernels read the lengths themselves, so the same workspace serves any
+ *     lengths within the block table.  Query the workspace size with the
+ *     device current that will run the call.
  */
 #ifndef MLA_H_
 #define MLA_H_

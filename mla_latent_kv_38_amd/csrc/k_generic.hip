@@ -3,6 +3,8 @@
 // for DeepSeek-V2 shapes lives in k_decode_mfma.hip.
 #include <cmath>
 
+#include <atomic>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -534,12 +536,31 @@ static void workspace_split(const mla_dims& d, const DecodePlan& plan, int32_t B
   *ws_tbl = reinterpret_cast<int64_t*>(static_cast<char*>(ws) + o_bytes + l_bytes);
 }
 
+int device_cu_count() {
+  constexpr int kMaxDev = 64;
+  static std::atomic<int> known[kMaxDev];            // 0: not asked yet
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    (void)hipGetLastError();                         // leave no error behind for a later launch check
+    return kNumCU;
+  }
+  int n = known[dev].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    n = kNumCU;
+  }
+  known[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
   DecodePlan p{};
   p.kernel = mfma_decode_supported(d) ? kDecodeH64 : fp8_decode_supported(d) ? kDecodeFp8 : kDecodeGeneric;
   p.head_groups = p.kernel == kDecodeH64 ? d.n_heads / 64 : p.kernel == kDecodeFp8 ? d.n_heads / 16 : d.n_heads;
   // one workgroup per CU for the MFMA kernels; the generic kernel runs 4 per CU
-  int32_t autos = p.kernel != kDecodeGeneric ? (kNumCU / p.head_groups) : (kNumCU * 4) / d.n_heads;
+  const int32_t cus = device_cu_count();
+  int32_t autos = p.kernel != kDecodeGeneric ? (cus / p.head_groups) : (cus * 4) / d.n_heads;
   p.parts = num_splits > 0 ? num_splits : (autos > 0 ? autos : 1);
   const size_t slots = (size_t)p.parts + batch;
   size_t o_bytes = slots * d.n_heads * d.d_latent * sizeof(float);

@@ -5,8 +5,12 @@
 
 namespace mla {
 
-// Number of compute units the launch geometry is planned for (MI355X).
+// Compute units the launch geometry is planned for when the runtime cannot
+// report them (MI355X: 256).
 constexpr int kNumCU = 256;
+// Compute units of the current device (a partitioned MI355X reports fewer),
+// queried once per device; kNumCU when there is no device to ask.
+int device_cu_count();
 
 // An append carried by the absorb_q launch (mla_absorb_q_append).
 struct AppendArgs {
