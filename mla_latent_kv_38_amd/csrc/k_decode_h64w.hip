@@ -386,13 +386,22 @@ template <int TH>
 __device__ __forceinline__ void take_and_store(const Acc& acc, float sc, float sc_p, const LDSP float* xch,
                                                const Lane& ln, bool whole, uint16_t* dst) {
   const LDSP float* src = xch + TH * (8 * 16 * 64);
+  // every read of the partner's blocks goes out before the first use: the
+  // accumulator reads below are volatile asm, which the compiler does not
+  // move loads across, so reads left inside the loop would each wait their
+  // full LDS latency
+  f32x4 tp[8][4];
+#pragma unroll
+  for (int c = 0; c < 8; ++c)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) tp[c][r4] = *(const LDSP f32x4*)(src + ((c * 4 + r4) * 64 + ln.lane) * 4);
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     constexpr int kCb0 = 8 * TH;
     float v[16];
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4 t = *(const LDSP f32x4*)(src + ((c * 4 + r4) * 64 + ln.lane) * 4);
+      const f32x4 t = tp[c][r4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) v[4 * r4 + e] = __builtin_fmaf(agpr_read(acc.o[kCb0 + c][4 * r4 + e]), sc, t[e] * sc_p);
     }
