@@ -103,22 +103,28 @@ def test_split_partials_stay_near_the_unsplit_result(name):
     assert np.abs(la - lb).max() <= 1e-5 * max(1.0, np.abs(lb).max())
 
 
-@pytest.mark.parametrize("name", ["v2_b16_4k", "ragged_b64"])
+@pytest.mark.parametrize("name", list(CASES))
 def test_full_size_every_sequence_and_head(name):
     """Every (sequence, head) of the batch at full size against the oracle's
     latent-space decode (keybo.xyz page, section "第二步，推理时的吸收": scores
     over the latent rows, latent-space weighted sum) on the oracle's absorbed
-    queries and the rows as stored; the absorbed form itself is pinned to the
-    explicit one in the oracle's own tests.  Tolerance as for the sampled
-    outputs (bf16: 1e-2 of max|o_lat| per sequence, lse within 1e-2)."""
+    queries and the rows as stored (E4M3: the oracle's own codes times its
+    scales, which the device's codes match); the absorbed form itself is
+    pinned to the explicit one in the oracle's own tests.  Tolerance as for
+    the sampled outputs (bf16: 1e-2 of max|o_lat| per sequence, E4M3 cache
+    3e-2; lse to the same bound)."""
     w = W.make(name)
-    print(f"[fullsize all heads] {name}: B={w.B} tokens={w.total_tokens()}", flush=True)
+    print(f"[fullsize all heads] {name}: B={w.B} n_h={w.n_h} tokens={w.total_tokens()} kv={w.kv}", flush=True)
     res = C.run_chain(w)
     q_ref = O.absorb_q(w.q_c, w.q_r, w.w_uk, w.q_pos, w.rope_base)
     o_all, l_all = C.f64(res["o_lat"]), C.f64(res["lse"])
-    tol = C.TOL[w.act]
+    tol = C.TOL["e4m3" if w.kv == "e4m3" else w.act]
+    worst_o = worst_l = 0.0
     for b in range(w.B):
         rows = C.oracle_rows(w, b)["stored"]
         ref = O.latent_decode(q_ref[b], rows, w.d_c, w.scale)
-        assert C.rel_err(o_all[b], ref["o_lat"]) <= tol, f"o_lat b={b}"
-        assert C.lse_err(l_all[b], ref["lse"]) <= tol, f"lse b={b}"
+        eo, el = C.rel_err(o_all[b], ref["o_lat"]), C.lse_err(l_all[b], ref["lse"])
+        worst_o, worst_l = max(worst_o, eo), max(worst_l, el)
+        assert eo <= tol, f"o_lat b={b}"
+        assert el <= tol, f"lse b={b}"
+    print(f"[fullsize all heads] {name}: worst o_lat {worst_o:.3e}, worst lse {worst_l:.3e} (tol {tol})", flush=True)
