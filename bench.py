@@ -53,7 +53,7 @@ def parse():
 # Kernel sources the stored HBM-traffic measurement depends on; the stored
 # figure is reported only while their hash matches.
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
-TRAFFIC_SOURCES = ["mla_latent_kv_38_amd/csrc/k_decode_h64w.hip", "mla_latent_kv_38_amd/csrc/k_decode_mfma.hip",
+TRAFFIC_SOURCES = ["mla_latent_kv_38_amd/csrc/k_decode_h64w.hip", "mla_latent_kv_38_amd/csrc/k_decode_e4m3_h64.hip",
                    "mla_latent_kv_38_amd/csrc/k_decode_fp8.hip", "mla_latent_kv_38_amd/csrc/mla_device.h"]
 
 

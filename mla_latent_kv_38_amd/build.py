@@ -11,7 +11,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB_NAME = "libmla_gfx950.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
-SOURCES = ["mla_api.hip", "k_generic.hip", "k_decode_mfma.hip", "k_decode_fp8.hip", "k_proj_mfma.hip",
+SOURCES = ["mla_api.hip", "k_generic.hip", "k_decode_e4m3_h64.hip", "k_decode_fp8.hip", "k_proj_mfma.hip",
            "k_kvproj.hip",
            "k_decode_h64w.hip", "probes.hip"]
 

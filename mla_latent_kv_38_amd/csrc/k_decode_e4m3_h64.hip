@@ -1,35 +1,32 @@
-// MFMA decode for DeepSeek-V2 shapes: d_c = 512, d_R = 64 (rows of 576),
-// 64-token pages, bfloat16 queries, a bfloat16 or E4M3 cache, n_h a
-// multiple of 64.  Source: keybo.xyz page, section "第二步，推理时的吸收"
-// (scores against the cached latent with the absorbed query, softmax, the
-// weighted latent sum) and dgblog.top page, section "3. 一个聪明的优化：上采样
-// 矩阵可以"吸收""; the E4M3 row is code x per-row scale, which factors out of
+// 64-head decode over an E4M3 cache at DeepSeek-V2 shapes: d_c = 512,
+// d_R = 64 (rows of 576 codes, one float32 scale per row), 64-token pages,
+// bfloat16 queries, n_h a multiple of 64.  Source: keybo.xyz page, section
+// "第二步，推理时的吸收" (scores against the cached latent with the absorbed
+// query, softmax, the weighted latent sum) and dgblog.top page, section
+// "3. 一个聪明的优化：上采样矩阵可以"吸收""; the E4M3 row is code x per-row scale
+// (keybo.xyz page, section "所以 cache 逻辑到底哪里要重写"), which factors out of
 // both contractions.
 //
 // Work decomposition.  The batch's pages are flattened and cut into parts
 // (see mla_device.h); one workgroup handles one part for 64 heads.  A
 // workgroup is 4 waves on one CU; it streams its pages HBM -> LDS with
-// direct-to-LDS loads (double-buffered) and every latent row is read from LDS
+// direct-to-LDS loads (double-buffered) and every code row is read from LDS
 // by all 64 heads:
 //   QK  wave w scores head block hb = w & 1 (32 heads) against token half
 //       th = w >> 1 of the page: S^T[32 tok x 32 heads] = C[32 x 576] Q^T,
-//       36 MFMA 32x32x16 bf16, Q^T resident in registers.
+//       36 MFMA 32x32x16 bf16 on 8-code groups converted exactly to bf16 in
+//       registers, Q^T resident in AGPRs; the row scale multiplies the scores.
 //   softmax  per head (one lane), page max shared between the two token-half
 //       waves through LDS; the reference max only moves when the page max
 //       exceeds it by 2^8 (scores are in log2 units), so rescaling the
-//       accumulators is rare; P is written to LDS as bf16.
+//       accumulators is rare; P times the row scale goes to LDS as bf16.
 //   PV  wave w accumulates O^T[128 latent columns x 64 heads] =
 //       V^T[128 x 64 tok] P^T[64 tok x 64 heads]: 32 MFMAs per page; V^T
-//       comes from the row-major tile through ds_read_b64_tr_b16, each V
-//       fragment feeding two head blocks.
-// LDS rows are padded to 73 x 16 B so that the QK reads (16 rows, same
-// 16-B column per phase) and the transposed PV reads (4 rows 4 apart x 32
-// columns per phase) are free of bank conflicts; the token order inside each
-// MFMA is permuted to match (it is a contraction index, so any order is exact).
-// E4M3 cache (decode_mfma_h64<true>): the same decomposition on code rows
-// padded to 592 B; QK reads 8-code groups and PV reads V^T with
-// ds_read_b64_tr_b8, each converted exactly to bf16 in registers before its
-// MFMA; the row scale multiplies the scores and P.
+//       comes from ds_read_b64_tr_b8 on the code rows, converted the same
+//       way, each V fragment feeding two head blocks.
+// Code rows are padded to 37 x 16 B in LDS, the queries (staged once per
+// segment) to 73 x 16 B; the token order inside each MFMA is permuted to
+// match the reads (it is a contraction index, so any order is exact).
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -49,8 +46,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kD = 576;
 constexpr int kDc = 512;
 constexpr int kBs = 64;
-constexpr int kRowB = 1168;                 // 1152 data bytes + 16 pad (73 x 16 B)
-constexpr int kPageB = kBs * kRowB;         // 74752 = 73 x 1 KiB
+constexpr int kRowB = 1168;                 // query row in LDS: 1152 bytes + 16 pad (73 x 16 B)
+constexpr int kPageB = kBs * kRowB;         // 74752 = 73 x 1 KiB: a page buffer (64 padded query rows)
 constexpr int kPtRowB = 144;                // P^T row: 64 bf16 + 16 pad
 constexpr float kTau = 8.0f;                // lazy-rescale threshold (log2 units)
 constexpr int kCodePageB = kBs * kD;        // 36864: one page of E4M3 codes in the cache
@@ -59,42 +56,26 @@ constexpr int kCodeRowsB = kBs * kRowC;     // 37888; the page's 64 float32 scal
 static_assert(kCodeRowsB + kBs * 4 <= kPageB, "an E4M3 page fits a page buffer");
 
 
-// Copy one 64-token page (64 x 1152 B) into the padded LDS tile: 73 direct
-// loads of 64 lanes x 16 B; LDS slot s = 64 k + lane holds row s / 73, 16-B
-// chunk s % 73 (chunk 72 is padding and re-reads chunk 0).  Wave w issues
-// loads k = w, w + 4, ...; the lane's (row, chunk) advances by 256 slots
-// = 3 rows + 37 chunks per load.
-struct DmaWalk {
-  int row, ch;
-  __device__ __forceinline__ void start(int wave, int lane) {
-    const int s0 = 64 * wave + lane;
-    row = s0 / 73;
-    ch = s0 - 73 * row;
-  }
-  __device__ __forceinline__ void issue(const char* __restrict__ src, LDSP char* dst, int k) {
-    const unsigned off = static_cast<unsigned>(row * (kD * 2) + (ch == 72 ? 0 : ch * 16));
-    dma16(src, off, dst + 1024 * k);
+// The head group's 64 absorbed query rows (64 x 1152 B, contiguous in q_abs)
+// go into a page buffer with rows padded to 73 x 16 B: 73 direct loads of
+// 64 lanes x 16 B, LDS slot s = 64 k + lane holding row s / 73, 16-B chunk
+// s % 73 (chunk 72 is padding and re-reads chunk 0).  Wave w issues loads
+// k = w, w + 4, ... (19 for wave 0, 18 for the others); the lane's (row,
+// chunk) advances by 256 slots = 3 rows + 37 chunks per load.  The offsets
+// are the same for every segment, so each lane's 19 are computed once per
+// workgroup and kept in AGPRs (free beside the queries).
+__device__ __forceinline__ int dma_count(int wave) { return wave == 0 ? 19 : 18; }
+
+__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&offa)[19]) {
+  const int s0 = 64 * wave + lane;
+  int row = s0 / 73, ch = s0 - 73 * (s0 / 73);
+#pragma unroll
+  for (int i = 0; i < 19; ++i) {
+    const uint32_t off = static_cast<uint32_t>(row * (kD * 2) + (ch == 72 ? 0 : ch * 16));
+    asm volatile("" : "=a"(offa[i]) : "0"(off));
     ch += 37;
     row += 3;
     if (ch >= 73) { ch -= 73; row += 1; }
-  }
-};
-
-__device__ __forceinline__ int dma_count(int wave) { return wave == 0 ? 19 : 18; }
-
-// The walk is the same for every page, so each lane's 19 source offsets are
-// computed once per workgroup and kept in AGPRs (free beside the queries);
-// issuing a load then costs one register move.
-__device__ __forceinline__ void dma_offsets(int wave, int lane, uint32_t (&offa)[19]) {
-  DmaWalk w;
-  w.start(wave, lane);
-#pragma unroll
-  for (int i = 0; i < 19; ++i) {
-    const uint32_t off = static_cast<uint32_t>(w.row * (kD * 2) + (w.ch == 72 ? 0 : w.ch * 16));
-    asm volatile("" : "=a"(offa[i]) : "0"(off));
-    w.ch += 37;
-    w.row += 3;
-    if (w.ch >= 73) { w.ch -= 73; w.row += 1; }
   }
 }
 
@@ -159,32 +140,6 @@ __device__ __forceinline__ f32x16 qk_page_e4m3(const LDSP char* __restrict__ ap,
   return S;
 }
 
-// S^T[32 tokens x 32 heads] = C[32 x 576] . Q^T for one wave: 36 MFMAs fed
-// from LDS four fragments ahead, Q^T read straight from AGPRs.  With kDma the
-// wave's share of the next page's direct loads is spread over the MFMAs.
-template <bool kDma>
-__device__ __forceinline__ f32x16 qk_page(const LDSP char* __restrict__ ap, const bf16x8 (&qf)[36],
-                                          const uint32_t (&offa)[19], const char* nsrc_u, uint32_t nbuf_u,
-                                          int wave) {
-  f32x16 S;
-  constexpr int kPre = 4;
-  bf16x8 af[kPre];
-#pragma unroll
-  for (int kb = 0; kb < kPre; ++kb) af[kb] = *(const LDSP bf16x8*)(ap + 32 * kb);
-#pragma unroll
-  for (int kb = 0; kb < 36; ++kb) {
-    if (kb == 0)                                                  // accumulator starts from the constant 0
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=v"(S) : "v"(af[0]), "a"(qf[0]));
-    else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(af[kb % kPre]), "a"(qf[kb]));
-    if (kb + kPre < 36) af[kb % kPre] = *(const LDSP bf16x8*)(ap + 32 * (kb + kPre));
-    if (kDma && (kb & 1) == 0) dma16_u(nsrc_u, offa[kb >> 1], nbuf_u + 1024 * (wave + 4 * (kb >> 1)));
-  }
-  if (kDma && wave == 0) dma16_u(nsrc_u, offa[18], nbuf_u + 1024 * (4 * 18));
-  asm volatile("s_nop 7\n s_nop 7\n s_nop 3" ::: "memory");       // MFMA result -> VALU
-  return S;
-}
-
 // Two page buffers, the P^T tile and the exchange area are separate LDS
 // objects: with every buffer reference static, the compiler can tell the
 // next page's direct loads never alias the current page's reads and adds no
@@ -200,7 +155,7 @@ __shared__ int32_t g_lens[256];                               // seq_lens, when 
 __shared__ __attribute__((aligned(16))) int32_t g_xneed[4];   // per wave: its page half needs a new reference
 
 struct Lane {                      // per-lane constants
-  int wave, lane, l32, hi, hb, th, hg_part;
+  int wave, lane, l32, hi, hb, th;
   int a_off, pt_row, tr_off;
 };
 
@@ -209,49 +164,38 @@ struct Acc {                       // per-segment running state of one wave
   float m_ref, l_own;
 };
 
-// One page: QK (+ the next page's loads), softmax, PV.
+// One page: the next page's loads, QK, softmax, PV.
 // buf (read) and nbuf (direct-load target) are __restrict__: the compiler
 // then knows the in-flight loads into nbuf never alias reads of buf and adds
 // no waits of its own (the explicit vmcnt + barrier at the top orders them).
 //
-// E4M3 cache (kE4M3): the buffers hold code rows of 592 B and the page's
-// scales; both contractions convert their fragments in registers, and the
-// per-token scale s_t multiplies the scores and P (row = s_t * codes).
-template <bool kE4M3>
+// The buffers hold code rows of 592 B and the page's scales; both
+// contractions convert their fragments in registers, and the per-token scale
+// s_t multiplies the scores and P (row = s_t * codes).
 __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict__ buf,
                                           LDSP char* __restrict__ nbuf,
                                           bool dma, const char* cbase, const int32_t* bt_after,
-                                          int32_t& pg_after, const uint32_t (&offa)[19],
-                                          const bf16x8 (&qf)[36], int nvalid, int lo, float s2, Acc& acc,
-                                          const char* sbase = nullptr) {
+                                          int32_t& pg_after, const bf16x8 (&qf)[36], int nvalid, int lo,
+                                          float s2, Acc& acc, const char* sbase) {
   LDSP char* pt = (LDSP char*)g_pt;
   float* xm = g_xm;
   float* xa = g_xa;
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();                                               // this page landed; previous one consumed
   asm volatile("" : "+v"(pg_after));                             // its load (one page ago) has landed
-  const char* nsrc_u = uniform(cbase + (int64_t)pg_after * (kE4M3 ? kCodePageB : kBs * kD * 2));   // next page
+  const char* nsrc_u = uniform(cbase + (int64_t)pg_after * kCodePageB);   // next page
   const uint32_t nbuf_u = uniform_lds(nbuf);
   const int32_t pg2 = bt_after ? *bt_after : 0;                  // page id two ahead, read during this page
 
-  if (kE4M3 && dma)                                               // next page's codes and scales, now
+  if (dma)                                                        // next page's codes and scales, now
     dma_code_page(nsrc_u, nbuf_u, sbase + (int64_t)pg_after * (kBs * 4), nbuf + kCodeRowsB, ln.wave, ln.lane);
 
-  // The two head groups of a part share an L2.  Waves of matching parity
-  // (wave & 1 == head group) load their half of the next page during QK, the
-  // other half is loaded during PV, by which time the partner workgroup's
-  // early half has reached the L2: each 128-B line comes from HBM once and
-  // each CU waits for HBM latency on only half of its page.
-  const bool early = (ln.wave & 1) == ln.hg_part;
-  f32x16 S;
-  if constexpr (kE4M3) S = qk_page_e4m3(buf + ln.a_off, qf);
-  else S = dma && early ? qk_page<true>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave)
-                        : qk_page<false>(buf + ln.a_off, qf, offa, nsrc_u, nbuf_u, ln.wave);
+  f32x16 S = qk_page_e4m3(buf + ln.a_off, qf);
 
   // E4M3: score_t = s_t (q . codes_t); the scale of a masked row is taken
   // as 0 so that whatever its slot holds cannot reach P.
   float sct[16];
-  if constexpr (kE4M3) {
+  {
     const LDSP float* sc = (const LDSP float*)(buf + kCodeRowsB);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -294,8 +238,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
       const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], s2, -acc.m_ref));
       const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], s2, -acc.m_ref));
       ps += p0 + p1;
-      if constexpr (kE4M3) pk[r >> 1] = pack2_bf16(p0 * sct[r], p1 * sct[r + 1]);
-      else pk[r >> 1] = pack2_bf16(p0, p1);
+      pk[r >> 1] = pack2_bf16(p0 * sct[r], p1 * sct[r + 1]);
     }
 #pragma unroll
     for (int ra = 0; ra < 4; ++ra) {
@@ -304,19 +247,11 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
     }
   };
   make_p();
-  if (nvalid < kBs || lo > 0) {                                  // masked rows: zero the latent
-    if constexpr (kE4M3) {
-      for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 32; i += 256) {
-        const int k = i >> 5, ch = i & 31;
-        const int row = k < lo ? k : nvalid + (k - lo);
-        *(LDSP u32x4*)(buf + row * kRowC + ch * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
-    } else {
-      for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 64; i += 256) {
-        const int k = i >> 6, ch = i & 63;
-        const int row = k < lo ? k : nvalid + (k - lo);
-        *(LDSP u32x4*)(buf + row * kRowB + ch * 16) = u32x4{0u, 0u, 0u, 0u};
-      }
+  if (nvalid < kBs || lo > 0) {                                  // masked rows: zero the latent codes
+    for (int i = threadIdx.x; i < (kBs - nvalid + lo) * 32; i += 256) {
+      const int k = i >> 5, ch = i & 31;
+      const int row = k < lo ? k : nvalid + (k - lo);
+      *(LDSP u32x4*)(buf + row * kRowC + ch * 16) = u32x4{0u, 0u, 0u, 0u};
     }
   }
   barrier_lds();                                                 // P^T, page maxima and flags visible
@@ -326,23 +261,13 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   auto pload = [&](int ks, int h2) {
     return *(const LDSP bf16x8*)(pt + (32 * h2 + ln.l32) * kPtRowB + (16 * ks + 8 * ln.hi) * 2);
   };
-  auto vraw = [&](int step) {            // E4M3: V^T by transposed byte reads
+  auto vraw = [&](int step) {            // V^T by transposed byte reads
     const int ks = step >> 2, cb = step & 3;
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr8_b64_v2i32(
                                          (LDSP i32x2*)(vbase + 16 * ks * kRowC + 32 * cb)));
   };
-  auto vload = [&](int step) {           // bf16: V^T by transposed 16-bit reads
-    const int ks = step >> 2, cb = step & 3;
-    const LDSP char* vp = vbase + 16 * ks * kRowB + 64 * cb;
-    const s16x4 v0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)vp);
-    const s16x4 v1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDSP s16x4*)(vp + kRowB));
-    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-  };
   const u32x4 flags = *(const LDSP u32x4*)g_xneed;
-  u32x2 rcur{};
-  bf16x8 vcur{};
-  if constexpr (kE4M3) rcur = vraw(0);
-  else vcur = vload(0);
+  u32x2 rcur = vraw(0);
   bf16x8 pc0 = pload(0, 0), pc1 = pload(0, 1);
   const bool slow = (flags[0] | flags[1] | flags[2] | flags[3]) != 0;
   float alpha = 1.f;
@@ -369,7 +294,7 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
       for (int r = 0; r < 16; ++r) { acc.o[cb][0][r] *= al0; acc.o[cb][1][r] *= al1; }
     asm volatile("s_nop 2" ::: "memory");                        // VALU -> MFMA source
   }
-  if constexpr (kE4M3) {                 // V^T converted before each MFMA pair
+  {                                      // V^T converted before each MFMA pair
     bf16x8 pn0 = pc0, pn1 = pc1;
 #pragma unroll
     for (int step = 0; step < 16; ++step) {
@@ -384,33 +309,11 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
       rcur = rnext;
       if (cb == 3) { pc0 = pn0; pc1 = pn1; }
     }
-    pg_after = pg2;
-    return;
-  }
-  bf16x8 pn0 = pc0, pn1 = pc1;
-#pragma unroll
-  for (int step = 0; step < 16; ++step) {
-    const int cb = step & 3;
-    bf16x8 vnext = vcur;
-    if (step + 1 < 16) vnext = vload(step + 1);
-    if (cb == 0 && step + 4 < 16) { pn0 = pload((step >> 2) + 1, 0); pn1 = pload((step >> 2) + 1, 1); }
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %2, %3, %0\n"
-                 "v_mfma_f32_32x32x16_bf16 %1, %2, %4, %1"
-                 : "+v"(acc.o[cb][0]), "+v"(acc.o[cb][1]) : "v"(vcur), "v"(pc0), "v"(pc1));
-    if (!kE4M3 && dma && !early) dma16_u(nsrc_u, offa[step], nbuf_u + 1024 * (ln.wave + 4 * step));
-    vcur = vnext;
-    if (cb == 3) { pc0 = pn0; pc1 = pn1; }
-  }
-  if (!kE4M3 && dma && !early) {
-    dma16_u(nsrc_u, offa[16], nbuf_u + 1024 * (ln.wave + 64));
-    dma16_u(nsrc_u, offa[17], nbuf_u + 1024 * (ln.wave + 68));
-    if (ln.wave == 0) dma16_u(nsrc_u, offa[18], nbuf_u + 1024 * 72);
   }
   pg_after = pg2;
 }
 
-template <bool kE4M3>
-__global__ void __launch_bounds__(256, 1) decode_mfma_h64(
+__global__ void __launch_bounds__(256, 1) decode_e4m3_h64(
     int32_t B, int32_t n_h, int32_t W, int32_t HG, float s2,
     const uint16_t* __restrict__ q_abs, const void* __restrict__ cache, const float* __restrict__ kv_scale,
     const int32_t* __restrict__ block_table, int32_t max_pages, int32_t bt_div,
@@ -433,7 +336,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   const int ppx = (W + 7) / 8;
   const int xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
   const int hg = j % HG;
-  ln.hg_part = hg & 1;
   const int part = xcd * ppx + j / HG;
   if (part >= W) return;
 
@@ -441,25 +343,21 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   {
     const int i = ln.l32, a = i >> 3, q = i & 3, bq = (i >> 2) & 1;
     const int tok = 32 * ln.th + 16 * (a >> 1) + 2 * (a & 1) + bq + 4 * q;
-    ln.a_off = kE4M3 ? tok * kRowC + ln.hi * 16 : tok * kRowB + ln.hi * 16;
+    ln.a_off = tok * kRowC + ln.hi * 16;
   }
   ln.pt_row = (ln.hb * 32 + ln.l32) * kPtRowB;
   {
-    const int g = ln.lane >> 4, sg = ln.lane & 15;             // PV transposed reads
-    ln.tr_off = (4 * (sg >> 2) + 2 * ln.hi) * kRowB + (128 * ln.wave + 16 * (g & 1) + 4 * (sg & 3)) * 2;
-    if (kE4M3) {
-      // transposed byte reads: within a 16-lane group, source lane sg names
-      // token row T(sg / 2) and the 8 codes at column 16 (g & 1) + 8 (sg & 1)
-      // of the wave's block; lane s then receives column 16 (g & 1) + s of
-      // rows T(0..7), the token order of the P^T slots 8 hi .. 8 hi + 7:
-      // T(e) = 4 (e & 3) + 2 hi + e / 4.
-      const int e = sg >> 1;
-      ln.tr_off = (4 * (e & 3) + 2 * ln.hi + (e >> 2)) * kRowC + 128 * ln.wave + 16 * (g & 1) + 8 * (sg & 1);
-    }
+    // PV transposed byte reads: within a 16-lane group, source lane sg names
+    // token row T(sg / 2) and the 8 codes at column 16 (g & 1) + 8 (sg & 1)
+    // of the wave's block; lane s then receives column 16 (g & 1) + s of
+    // rows T(0..7), the token order of the P^T slots 8 hi .. 8 hi + 7:
+    // T(e) = 4 (e & 3) + 2 hi + e / 4.
+    const int g = ln.lane >> 4, sg = ln.lane & 15, e = sg >> 1;
+    ln.tr_off = (4 * (e & 3) + 2 * ln.hi + (e >> 2)) * kRowC + 128 * ln.wave + 16 * (g & 1) + 8 * (sg & 1);
   }
 
   // (these do not depend on the part: computed while the locator's load is in flight)
-  uint32_t offa[19];                                             // this lane's page-load offsets (AGPRs)
+  uint32_t offa[19];                                             // this lane's query-load offsets (AGPRs)
   dma_offsets(ln.wave, ln.lane, offa);
   const int ndma = dma_count(ln.wave);
 
@@ -473,7 +371,6 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
   int64_t first = pr.first;
   const char* cbase = reinterpret_cast<const char*>(cache);
   const char* sbase = reinterpret_cast<const char*>(kv_scale);
-  constexpr int64_t kPageBytesG = kE4M3 ? (int64_t)kCodePageB : (int64_t)kBs * kD * 2;
 
   for (;;) {
     // The window [st, L) of sequence b: its pages start at page fp; L and the
@@ -492,8 +389,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
     }
 
     // First page into buffer 0 and this head group's 64 absorbed query rows
-    // (contiguous in q_abs, the same 64 x 1152 B shape as a page) into buffer
-    // 1, both as whole 1 KiB direct loads (an E4M3 page by its own walk).
+    // (contiguous in q_abs, 64 x 1152 B) into buffer 1, both by 1 KiB direct
+    // loads (the page by its own walk).
     int32_t pg0, pg_next;
     Acc acc;                                                     // cleared while the first loads are in flight
 #pragma unroll
@@ -513,27 +410,15 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       // ids of the first two pages in one round trip (the second is read only
       // when the segment has it)
       sload2_i32(bt + jp0, bt + (jp0 + 1 < jp1 ? jp0 + 1 : jp0), &pg0, &pg_next);
-      const char* src_u = uniform(cbase + (int64_t)pg0 * kPageBytesG);
-      if constexpr (kE4M3) {
-        dma_code_page(src_u, uniform_lds((LDSP char*)g_page0), sbase + (int64_t)pg0 * (kBs * 4),
-                      (LDSP char*)g_page0 + kCodeRowsB, ln.wave, ln.lane);
-      } else {
-        const uint32_t p_m0 = uniform_lds((LDSP char*)g_page0);
-#pragma unroll
-        for (int i = 0; i < 19; ++i)
-          if (i < ndma) dma16_u(src_u, offa[i], p_m0 + 1024 * (ln.wave + 4 * i));
-      }
+      const char* src_u = uniform(cbase + (int64_t)pg0 * kCodePageB);
+      dma_code_page(src_u, uniform_lds((LDSP char*)g_page0), sbase + (int64_t)pg0 * (kBs * 4),
+                    (LDSP char*)g_page0 + kCodeRowsB, ln.wave, ln.lane);
     }
     // Wait for this wave's query loads only (issued before the page's, and
     // direct loads complete in order): the first page keeps landing while
     // the queries are read into registers; its own wait is at the page top.
-    if constexpr (kE4M3) {
-      if (ln.wave == 0) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
-    } else {
-      if (ndma == 19) asm volatile("s_waitcnt vmcnt(19)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(18)" ::: "memory");
-    }
+    if (ln.wave == 0) asm volatile("s_waitcnt vmcnt(11)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
     barrier_lds();
     // Q^T fragments stay in AGPRs for the whole segment (the MFMAs read them there)
     bf16x8 qf[36];
@@ -541,9 +426,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       const LDSP char* qrow = (LDSP char*)g_page1 + (ln.hb * 32 + ln.l32) * kRowB;
       bf16x8 t[36];
 #pragma unroll
-      for (int kb = 0; kb < 36; ++kb)               // contraction order of qk_page / qk_page_e4m3
-        t[kb] = *(const LDSP bf16x8*)(qrow + (kE4M3 ? 64 * (kb >> 1) + 32 * ln.hi + 16 * (kb & 1)
-                                                    : 32 * kb + 16 * ln.hi));
+      for (int kb = 0; kb < 36; ++kb)               // contraction order of qk_page_e4m3
+        t[kb] = *(const LDSP bf16x8*)(qrow + 64 * (kb >> 1) + 32 * ln.hi + 16 * (kb & 1));
 #pragma unroll
       for (int kb = 0; kb < 36; ++kb) asm volatile("" : "=a"(qf[kb]) : "0"(t[kb]));
     }
@@ -561,8 +445,8 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
       LDSP char* nbuf = even ? (LDSP char*)g_page1 : (LDSP char*)g_page0;
       const int nvalid = min(kBs, Lu - jp * kBs);                 // jp * 64 < L: no overflow
       const bool more = jp + 1 < j1;
-      page_step<kE4M3>(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, offa, qf,
-                       nvalid, jp == 0 ? lo : 0, s2, acc, sbase);
+      page_step(ln, buf, nbuf, more, cbase, jp + 2 < j1 ? bt + jp + 2 : nullptr, pg_next, qf, nvalid,
+                jp == 0 ? lo : 0, s2, acc, sbase);
     }
 
     // ---- segment epilogue: normalise and store ------------------------------
@@ -627,7 +511,7 @@ __global__ void __launch_bounds__(256, 1) decode_mfma_h64(
 }
 
 // ---------------------------------------------------------------------------
-// Merge of the split-KV partials of decode_mfma_h64.  A partial (slot, 64-head
+// Merge of the split-KV partials of decode_e4m3_h64.  A partial (slot, 64-head
 // group) is 64 KiB of bfloat16 in register order: quad (w*4 + cb)*4 + q4
 // holds, for lane l, 16 B: latent columns 128w + 32cb + 8q4 + 4(l/32) .. +3
 // of head l%32, then the same columns of head 32 + l%32, already divided by
@@ -730,24 +614,23 @@ __global__ void __launch_bounds__(256) combine_h64(int32_t B, int32_t n_h, int32
 
 }  // namespace
 
-bool mfma_decode_supported(const mla_dims& d) {
-  return d.act_dtype == MLA_BF16 && (d.kv_dtype == MLA_BF16 || d.kv_dtype == MLA_E4M3) && d.d_latent == kDc &&
-         d.d_rope == 64 && d.block_size == kBs && d.n_heads % 64 == 0;
+bool e4m3_h64_decode_supported(const mla_dims& d) {
+  return d.act_dtype == MLA_BF16 && d.kv_dtype == MLA_E4M3 && d.d_latent == kDc && d.d_rope == 64 &&
+         d.block_size == kBs && d.n_heads % 64 == 0;
 }
 
-hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
-                              const void* q_abs, const void* cache, const float* kv_scale,
-                              const int32_t* block_table, int32_t max_pages, int32_t bt_div,
-                              const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
-                              float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s) {
+hipError_t launch_decode_e4m3_h64(const mla_dims& d, const DecodePlan& plan, int32_t B,
+                                  const void* q_abs, const void* cache, const float* kv_scale,
+                                  const int32_t* block_table, int32_t max_pages, int32_t bt_div,
+                                  const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
+                                  float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s) {
   const int HG = d.n_heads / 64;
   const int W = plan.parts;
   const int grid = ((W + 7) / 8) * 8 * HG;                  // 8 XCDs x ceil(W/8) parts x HG
   const float s2 = d.softmax_scale * 1.4426950408889634f;
-  auto kern = d.kv_dtype == MLA_E4M3 ? decode_mfma_h64<true> : decode_mfma_h64<false>;
-  kern<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs), cache, kv_scale,
-                            block_table, max_pages, bt_div, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl,
-                            static_cast<uint16_t*>(o_lat), lse);
+  decode_e4m3_h64<<<grid, 256, 0, s>>>(B, d.n_heads, W, HG, s2, static_cast<const uint16_t*>(q_abs), cache,
+                                       kv_scale, block_table, max_pages, bt_div, seq_lens, seq_starts, ws_o,
+                                       ws_lse, ws_tbl, static_cast<uint16_t*>(o_lat), lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   combine_h64<<<B * HG * 16, 256, 0, s>>>(B, d.n_heads, W, HG, seq_lens, seq_starts, ws_o, ws_lse, ws_tbl,

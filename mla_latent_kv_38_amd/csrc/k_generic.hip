@@ -1,6 +1,7 @@
 // Generic kernels: any head/latent/RoPE widths, float32 or bfloat16 activations,
-// float32 / bfloat16 / E4M3 cache.  Plain FMA arithmetic; the MFMA decode path
-// for DeepSeek-V2 shapes lives in k_decode_mfma.hip.
+// float32 / bfloat16 / E4M3 cache.  Plain FMA arithmetic; the MFMA decode
+// kernels for DeepSeek-V2 shapes live in k_decode_h64w.hip (bf16 cache),
+// k_decode_e4m3_h64.hip and k_decode_fp8.hip (E4M3 cache).
 #include <cmath>
 
 #include <atomic>
@@ -556,7 +557,9 @@ int device_cu_count() {
 
 DecodePlan plan_decode(const mla_dims& d, int32_t batch, int32_t num_splits) {
   DecodePlan p{};
-  p.kernel = mfma_decode_supported(d) ? kDecodeH64 : fp8_decode_supported(d) ? kDecodeFp8 : kDecodeGeneric;
+  p.kernel = h64w_decode_supported(d) || e4m3_h64_decode_supported(d) ? kDecodeH64
+             : fp8_decode_supported(d)                              ? kDecodeFp8
+                                                                    : kDecodeGeneric;
   p.head_groups = p.kernel == kDecodeH64 ? d.n_heads / 64 : p.kernel == kDecodeFp8 ? d.n_heads / 16 : d.n_heads;
   // one workgroup per CU for the MFMA kernels; the generic kernel runs 4 per CU
   const int32_t cus = device_cu_count();
@@ -585,9 +588,9 @@ hipError_t launch_decode(const mla_dims& d, const DecodePlan& plan, int32_t B, c
   if (plan.kernel == kDecodeH64 && aligned && h64w_decode_supported(d))
     return launch_decode_h64w(d, plan, B, q_abs, cache, block_table, max_pages, bt_div, seq_lens, seq_starts, ws_o,
                               ws_lse, ws_tbl, o_lat, lse, s);
-  if (plan.kernel == kDecodeH64 && aligned &&
-      (d.kv_dtype != MLA_E4M3 || reinterpret_cast<uintptr_t>(kv_scale) % 4 == 0))
-    return launch_decode_mfma(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
+  if (plan.kernel == kDecodeH64 && aligned && e4m3_h64_decode_supported(d) &&
+      reinterpret_cast<uintptr_t>(kv_scale) % 4 == 0)
+    return launch_decode_e4m3_h64(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,
                               seq_starts, ws_o, ws_lse, ws_tbl, o_lat, lse, s);
   if (plan.kernel == kDecodeFp8 && aligned && reinterpret_cast<uintptr_t>(kv_scale) % 16 == 0)
     return launch_decode_fp8(d, plan, B, q_abs, cache, kv_scale, block_table, max_pages, bt_div, seq_lens,

@@ -76,9 +76,8 @@ hipError_t launch_absorb_q_mfma(const mla_dims& d, int32_t B, const void* q_c, c
 hipError_t launch_up_v_mfma(const mla_dims& d, int32_t B, const void* o_lat, const void* w_uv, void* out,
                             hipStream_t s, bool* handled);
 
-// Whether the MFMA decode kernels handle these dims (bf16 cache: 64-head
-// groups; E4M3 cache: 16-head groups).
-bool mfma_decode_supported(const mla_dims& d);
+// Whether the MFMA decode kernels handle these dims.  E4M3 cache in 16-head
+// groups (k_decode_fp8.hip, when n_h is not a multiple of 64):
 bool fp8_decode_supported(const mla_dims& d);
 hipError_t launch_decode_fp8(const mla_dims& d, const DecodePlan& plan, int32_t B, const void* q_abs,
                              const void* cache, const float* kv_scale, const int32_t* block_table,
@@ -92,10 +91,13 @@ hipError_t launch_decode_h64w(const mla_dims& d, const DecodePlan& plan, int32_t
                               const void* cache, const int32_t* block_table, int32_t max_pages, int32_t bt_div,
                               const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o, float* ws_lse,
                               int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s);
-hipError_t launch_decode_mfma(const mla_dims& d, const DecodePlan& plan, int32_t B,
-                              const void* q_abs, const void* cache, const float* kv_scale,
-                              const int32_t* block_table, int32_t max_pages, int32_t bt_div,
-                              const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
-                              float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s);
+// E4M3 cache at 64-head multiples, codes converted to bf16 in registers
+// (k_decode_e4m3_h64.hip).
+bool e4m3_h64_decode_supported(const mla_dims& d);
+hipError_t launch_decode_e4m3_h64(const mla_dims& d, const DecodePlan& plan, int32_t B,
+                                  const void* q_abs, const void* cache, const float* kv_scale,
+                                  const int32_t* block_table, int32_t max_pages, int32_t bt_div,
+                                  const int32_t* seq_lens, const int32_t* seq_starts, float* ws_o,
+                                  float* ws_lse, int64_t* ws_tbl, void* o_lat, float* lse, hipStream_t s);
 
 }  // namespace mla
