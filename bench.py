@@ -107,7 +107,7 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this build has no "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the library has no "
               f"multi-GPU path", file=sys.stderr)
         sys.exit(2)
     import torch

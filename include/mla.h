@@ -62,7 +62,7 @@ typedef enum {
   MLA_ERR_SHAPE = -2,       /* a size is out of range or unsupported */
   MLA_ERR_DTYPE = -3,       /* unknown dtype or unsupported combination */
   MLA_ERR_WORKSPACE = -4,   /* workspace smaller than mla_decode_workspace_bytes */
-  MLA_ERR_UNSUPPORTED = -5, /* valid request this build has no kernel for */
+  MLA_ERR_UNSUPPORTED = -5, /* valid request the library has no kernel for */
   MLA_ERR_HIP = -6          /* a HIP launch failed; see mla_last_hip_error() */
 } mla_status;
 

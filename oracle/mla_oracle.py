@@ -28,7 +28,7 @@ The explicit form below rebuilds k_C and v per head and runs ordinary softmax
 attention; the absorbed form (``absorbed_decode``/``latent_decode``) exists so
 the tests can check the absorption identity against it.
 
-Readings where the pages leave a step open (all listed in the design doc):
+Readings where the pages leave a step open:
   * q_R has one d_R-vector per head; k_R is one d_R-vector per token shared by
     all heads.
   * RoPE pairs dimensions (2i, 2i+1); theta_i = base^(-2i/d_R); positions are
