@@ -517,11 +517,58 @@ __global__ void __launch_bounds__(256, 1) decode_e4m3_h64(
 // of head l%32, then the same columns of head 32 + l%32, already divided by
 // the partial's own row sum; its log-sum-exp (float32) is in ws_lse.
 // Workgroup = (sequence, head group, wave-column block w*4+cb); thread
-// (q4, l) owns one 16-B chunk of each partial.  Parts are
-// merged eight at a time with a running maximum, every load of a batch in
-// flight at once and no LDS or barrier after the page count:
+// (q4, l) owns one 16-B chunk of each partial.  Parts are merged with a
+// running maximum, a batch of loads in flight at once and no LDS or barrier
+// after the page count:
 //   o_lat = sum_k e^(lse_k - M) o_k / sum_k e^(lse_k - M),  lse = M + ln(sum).
 // ---------------------------------------------------------------------------
+// Parts are merged kN at a time (2, 4 or 8 by the sequence's part count, so
+// that a sequence split in two or four parts issues no loads beyond its
+// parts), all kN loads of a batch in flight together; each thread carries
+// two heads (l32 and 32 + l32).
+struct MergeState2 {
+  f32x4 acc0, acc1;
+  float m0, m1, d0, d1;
+};
+
+template <int kN>
+__device__ __forceinline__ void merge_parts(MergeState2& st, int64_t w0, int64_t w1, int32_t b, int hg, int64_t P,
+                                            int32_t W, bool all_live, const uint16_t* __restrict__ ws16, int off,
+                                            const float* __restrict__ ws_lse, int32_t n_h, int l32) {
+  for (int64_t base = w0; base <= w1; base += kN) {
+    f32x4 v0[kN], v1[kN];
+    float e0[kN], e1[kN];
+#pragma unroll
+    for (int jj = 0; jj < kN; ++jj) {              // part w0 always holds a page: dead parts read it
+      const int64_t w = base + jj;
+      const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
+      const int64_t slot = (live ? w : w0) + b;
+      const u32x4 raw = *reinterpret_cast<const u32x4*>(ws16 + (slot * n_h + (int64_t)hg * 64) * kDc + off);
+      v0[jj] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+      v1[jj] = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
+                     __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
+      const float* ls = ws_lse + slot * n_h + (int64_t)hg * 64;
+      e0[jj] = live ? ls[l32] : -INFINITY;
+      e1[jj] = live ? ls[32 + l32] : -INFINITY;
+    }
+    float n0 = st.m0, n1 = st.m1;
+#pragma unroll
+    for (int jj = 0; jj < kN; ++jj) { n0 = fmaxf(n0, e0[jj]); n1 = fmaxf(n1, e1[jj]); }
+    const float a0 = n0 == st.m0 ? 1.f : __expf(st.m0 - n0), a1 = n1 == st.m1 ? 1.f : __expf(st.m1 - n1);
+    st.acc0 *= a0; st.d0 *= a0; st.m0 = n0;
+    st.acc1 *= a1; st.d1 *= a1; st.m1 = n1;
+#pragma unroll
+    for (int jj = 0; jj < kN; ++jj) {
+      const float x0 = e0[jj] == -INFINITY ? 0.f : __expf(e0[jj] - st.m0);
+      const float x1 = e1[jj] == -INFINITY ? 0.f : __expf(e1[jj] - st.m1);
+      st.d0 += x0; st.d1 += x1;
+      st.acc0 += x0 * v0[jj];
+      st.acc1 += x1 * v1[jj];
+    }
+  }
+}
+
 // One (sequence b, head group hg, wave-column block wc) of the merge.
 __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t n_h, int32_t W, int64_t P,
                                              int64_t np, int64_t w0, int64_t w1, const float* __restrict__ ws_o,
@@ -543,40 +590,13 @@ __device__ __forceinline__ void combine_item(int32_t b, int hg, int wc, int32_t 
   const bool all_live = P >= W;                    // every part holds a page unless parts outnumber pages
   const int off = (wc * 4 + q4) * 512 + lane * 8;
   const uint16_t* ws16 = reinterpret_cast<const uint16_t*>(ws_o);
-  f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  float m0 = -INFINITY, m1 = -INFINITY, d0 = 0.f, d1 = 0.f;
-  for (int64_t base = w0; base <= w1; base += 8) {
-    f32x4 v0[8], v1[8];
-    float e0[8], e1[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {               // part w0 always holds a page: dead parts read it
-      const int64_t w = base + jj;
-      const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
-      const int64_t slot = (live ? w : w0) + b;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(ws16 + (slot * n_h + (int64_t)hg * 64) * kDc + off);
-      v0[jj] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
-                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
-      v1[jj] = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
-                     __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
-      const float* ls = ws_lse + slot * n_h + (int64_t)hg * 64;
-      e0[jj] = live ? ls[l32] : -INFINITY;
-      e1[jj] = live ? ls[32 + l32] : -INFINITY;
-    }
-    float n0 = m0, n1 = m1;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) { n0 = fmaxf(n0, e0[jj]); n1 = fmaxf(n1, e1[jj]); }
-    const float a0 = n0 == m0 ? 1.f : __expf(m0 - n0), a1 = n1 == m1 ? 1.f : __expf(m1 - n1);
-    acc0 *= a0; d0 *= a0; m0 = n0;
-    acc1 *= a1; d1 *= a1; m1 = n1;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float x0 = e0[jj] == -INFINITY ? 0.f : __expf(e0[jj] - m0);
-      const float x1 = e1[jj] == -INFINITY ? 0.f : __expf(e1[jj] - m1);
-      d0 += x0; d1 += x1;
-      acc0 += x0 * v0[jj];
-      acc1 += x1 * v1[jj];
-    }
-  }
+  MergeState2 st{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, -INFINITY, -INFINITY, 0.f, 0.f};
+  const int64_t nparts = w1 - w0 + 1;              // the same for the whole workgroup
+  if (nparts <= 2) merge_parts<2>(st, w0, w1, b, hg, P, W, all_live, ws16, off, ws_lse, n_h, l32);
+  else if (nparts <= 4) merge_parts<4>(st, w0, w1, b, hg, P, W, all_live, ws16, off, ws_lse, n_h, l32);
+  else merge_parts<8>(st, w0, w1, b, hg, P, W, all_live, ws16, off, ws_lse, n_h, l32);
+  const f32x4 acc0 = st.acc0, acc1 = st.acc1;
+  const float m0 = st.m0, m1 = st.m1, d0 = st.d0, d1 = st.d1;
   const int col = col0 + 8 * q4 + 4 * (lane >> 5);
   const float i0 = 1.f / d0, i1 = 1.f / d1;
   *reinterpret_cast<u32x2*>(o_lat + (head0 + l32) * kDc + col) =

@@ -682,10 +682,55 @@ __global__ void __launch_bounds__(256, 1) decode_h64w(
 // group) is 64 KiB of bfloat16 in the register order above, already divided
 // by its own row sum; its log-sum-exp (float32) is in ws_lse.  One workgroup
 // per (sequence, head group, 4 of the 64 chunks); thread (wave q4, lane l)
-// owns one 16-B piece of each partial.  Parts are merged eight at a time with
-// a running maximum:
+// owns one 16-B piece of each partial.  Parts are merged kN at a time with a
+// running maximum, all kN loads of a batch in flight together:
 //   o_lat = sum_k e^(lse_k - M) o_k / sum_k e^(lse_k - M),  lse = M + ln(sum).
+// kN is 2, 4 or 8 by the sequence's part count, so that a sequence split in
+// two or four parts (ragged batches, several query tokens) issues no loads
+// beyond its parts.
 // ---------------------------------------------------------------------------
+struct MergeState {
+  f32x4 a0, a1;
+  float m, d;
+};
+
+template <int kN>
+__device__ __forceinline__ void merge_parts(MergeState& st, int64_t w0, int64_t w1, int32_t b, int64_t P, int32_t W,
+                                            bool all_live, const uint16_t* __restrict__ ws16, int64_t off,
+                                            const float* __restrict__ lse_col, int32_t n_h) {
+  for (int64_t base = w0; base <= w1; base += kN) {
+    f32x4 v0[kN], v1[kN];
+    float e[kN];
+#pragma unroll
+    for (int jj = 0; jj < kN; ++jj) {                 // part w0 always holds a page: dead parts read it
+      const int64_t w = base + jj;
+      const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
+      const int64_t slot = (live ? w : w0) + b;
+      const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ws16 + slot * n_h * kDc + off));
+      v0[jj] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
+                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
+      v1[jj] = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
+                     __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
+      e[jj] = live ? lse_col[slot * n_h] : -INFINITY;
+    }
+    float n = st.m;
+#pragma unroll
+    for (int jj = 0; jj < kN; ++jj) n = fmaxf(n, e[jj]);
+    const float a = n == st.m ? 1.f : __expf(st.m - n);
+    st.a0 *= a;
+    st.a1 *= a;
+    st.d *= a;
+    st.m = n;
+#pragma unroll
+    for (int jj = 0; jj < kN; ++jj) {
+      const float x = e[jj] == -INFINITY ? 0.f : __expf(e[jj] - st.m);
+      st.d += x;
+      st.a0 += x * v0[jj];
+      st.a1 += x * v1[jj];
+    }
+  }
+}
+
 __global__ void __launch_bounds__(256) combine_h64w(int32_t B, int32_t n_h, int32_t W, int32_t HG,
                                                     const int32_t* __restrict__ seq_lens,
                                                     const int32_t* __restrict__ seq_starts,
@@ -734,39 +779,14 @@ __global__ void __launch_bounds__(256) combine_h64w(int32_t B, int32_t n_h, int3
   const bool all_live = P >= W;
   const uint16_t* ws16 = reinterpret_cast<const uint16_t*>(ws_o);
   const int64_t off = (int64_t)hg * 64 * kDc + (c * 64 + lane) * 8;
-  f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-  float m = -INFINITY, d = 0.f;
-  for (int64_t base = w0; base <= w1; base += 8) {
-    f32x4 v0[8], v1[8];
-    float e[8];
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {                  // part w0 always holds a page: dead parts read it
-      const int64_t w = base + jj;
-      const bool live = w <= w1 && (all_live || part_start(w, P, W) < part_start(w + 1, P, W));
-      const int64_t slot = (live ? w : w0) + b;
-      const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ws16 + slot * n_h * kDc + off));
-      v0[jj] = f32x4{__uint_as_float(raw.x << 16), __uint_as_float(raw.x & 0xffff0000u),
-                     __uint_as_float(raw.y << 16), __uint_as_float(raw.y & 0xffff0000u)};
-      v1[jj] = f32x4{__uint_as_float(raw.z << 16), __uint_as_float(raw.z & 0xffff0000u),
-                     __uint_as_float(raw.w << 16), __uint_as_float(raw.w & 0xffff0000u)};
-      e[jj] = live ? ws_lse[slot * n_h + (int64_t)hg * 64 + hh] : -INFINITY;
-    }
-    float n = m;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) n = fmaxf(n, e[jj]);
-    const float a = n == m ? 1.f : __expf(m - n);
-    a0 *= a;
-    a1 *= a;
-    d *= a;
-    m = n;
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {
-      const float x = e[jj] == -INFINITY ? 0.f : __expf(e[jj] - m);
-      d += x;
-      a0 += x * v0[jj];
-      a1 += x * v1[jj];
-    }
-  }
+  const float* lse_col = ws_lse + (int64_t)hg * 64 + hh;
+  MergeState st{{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, -INFINITY, 0.f};
+  const int64_t nparts = w1 - w0 + 1;                 // wave-uniform: one branch for the workgroup
+  if (nparts <= 2) merge_parts<2>(st, w0, w1, b, P, W, all_live, ws16, off, lse_col, n_h);
+  else if (nparts <= 4) merge_parts<4>(st, w0, w1, b, P, W, all_live, ws16, off, lse_col, n_h);
+  else merge_parts<8>(st, w0, w1, b, P, W, all_live, ws16, off, lse_col, n_h);
+  const f32x4 a0 = st.a0, a1 = st.a1;
+  const float m = st.m, d = st.d;
   const float inv = 1.f / d;
   *reinterpret_cast<u32x2*>(o_lat + head * kDc + col) =
       u32x2{pack2_bf16(a0[0] * inv, a0[1] * inv), pack2_bf16(a0[2] * inv, a0[3] * inv)};
