@@ -93,6 +93,20 @@ def test_ragged_shuffled_pages_any_split(splits):
     _check_all(w, res, heads=[0, 1, 63, 127])
 
 
+@pytest.mark.parametrize("name", ["ragged_b64", "v2_b16_4k_e4m3"])
+def test_merge_every_batch_width(name):
+    """One page per part (num_splits = total pages), so each sequence has as
+    many parts as pages: 1 (written whole), 2 (merged two at a time), 3 and
+    4 (four at a time, one dead slot for 3), 7 and 17 (eight at a time, 17
+    over three batches with dead slots), on the 64-head bf16 and E4M3 merges."""
+    pages = [1, 2, 3, 4, 7, 17]
+    lens = [64 * p - (13 if p > 1 else 0) for p in pages]      # ragged last pages
+    w = W.make(name, B=len(lens), lens=lens, n_h=128, shuffle=True)
+    assert int(w.num_pages) == sum(pages)
+    res = C.run_chain(w, num_splits=sum(pages))
+    _check_all(w, res, heads=[0, 31, 64, 127])
+
+
 def test_page_permutation_is_bitwise_invariant():
     import copy
     a = W.make("ragged_b64", B=3, lens=[200, 450, 130], shuffle=False)
