@@ -230,20 +230,27 @@ __device__ __forceinline__ void page_step(const Lane& ln, LDSP char* __restrict_
   const int need = __any(mloc > acc.m_ref + kTau);
   if (ln.lane == 0) g_xneed[ln.wave] = need;
   float ps = 0.f;
+  // P^T slot order: within each 16-token k-step, slot 8 h + e holds token
+  // 2 e + h, so that the transposed V reads of one lane half touch rows of one
+  // parity (conflict-free banks, see tr_off).  Score register r is token
+  // 16 (r >> 3) + 2 ((r >> 2) & 1) + hi + 4 (r & 3) of the wave's half, so a
+  // lane's 8 registers 8 kb .. 8 kb + 7 fill slots 8 hi .. 8 hi + 7 of k-step
+  // 2 th + kb in the order r = 8 kb + {0, 4, 1, 5, 2, 6, 3, 7}: one 16-B write.
   auto make_p = [&]() {
-    uint32_t pk[8];
     ps = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r], s2, -acc.m_ref));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r + 1], s2, -acc.m_ref));
-      ps += p0 + p1;
-      pk[r >> 1] = pack2_bf16(p0 * sct[r], p1 * sct[r + 1]);
-    }
+    for (int kb = 0; kb < 2; ++kb) {
+      uint32_t pk[4];
 #pragma unroll
-    for (int ra = 0; ra < 4; ++ra) {
-      const int slot = 16 * (2 * ln.th + (ra >> 1)) + 4 * (2 * (ra & 1) + ln.hi);
-      *(LDSP u32x2*)(pt + ln.pt_row + slot * 2) = u32x2{pk[2 * ra], pk[2 * ra + 1]};
+      for (int q = 0; q < 4; ++q) {
+        const int r0 = 8 * kb + q, r1 = r0 + 4;
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r0], s2, -acc.m_ref));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(S[r1], s2, -acc.m_ref));
+        ps += p0 + p1;
+        pk[q] = pack2_bf16(p0 * sct[r0], p1 * sct[r1]);
+      }
+      const int slot = 16 * (2 * ln.th + kb) + 8 * ln.hi;
+      *(LDSP u32x4*)(pt + ln.pt_row + slot * 2) = u32x4{pk[0], pk[1], pk[2], pk[3]};
     }
   };
   make_p();
@@ -351,9 +358,11 @@ __global__ void __launch_bounds__(256, 1) decode_e4m3_h64(
     // token row T(sg / 2) and the 8 codes at column 16 (g & 1) + 8 (sg & 1)
     // of the wave's block; lane s then receives column 16 (g & 1) + s of
     // rows T(0..7), the token order of the P^T slots 8 hi .. 8 hi + 7:
-    // T(e) = 4 (e & 3) + 2 hi + e / 4.
+    // T(e) = 2 e + hi.  Rows of one parity, 592 B = 148 banks apart, start
+    // 8 banks apart modulo 64, so the two 16-lane groups of a lane half
+    // (columns 0-15 and 16-31, 4 banks apart) cover the 64 banks once.
     const int g = ln.lane >> 4, sg = ln.lane & 15, e = sg >> 1;
-    ln.tr_off = (4 * (e & 3) + 2 * ln.hi + (e >> 2)) * kRowC + 128 * ln.wave + 16 * (g & 1) + 8 * (sg & 1);
+    ln.tr_off = (2 * e + ln.hi) * kRowC + 128 * ln.wave + 16 * (g & 1) + 8 * (sg & 1);
   }
 
   // (these do not depend on the part: computed while the locator's load is in flight)
