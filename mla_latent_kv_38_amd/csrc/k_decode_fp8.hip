@@ -9,19 +9,22 @@
 // to P in float32.
 //
 // Pages stream HBM -> LDS by direct loads through a ring of four slots
-// (codes in rows padded to 37 x 16 B, plus the 64 scales), three pages ahead
-// of the one being computed.  Wave w owns tokens 16w..16w+15 of every page
-// with its own online softmax state, so no score or maximum crosses waves
-// and a page needs one barrier:
-//   QK  S^T[16 tok x 16 heads] = C . Q^T: 18 v_mfma_f32_16x16x32_bf16, the A
-//       fragments read as 8 codes per lane and converted in registers, Q^T in
-//       AGPRs;
-//   PV  O^T[512 x 16 heads] += V^T[512 x 16 tok] . P^T: 32
-//       v_mfma_f32_16x16x16_bf16 with accumulators in AGPRs; V^T comes from
-//       ds_read_b64_tr_b8 (one read gives two 16-column blocks of the wave's
-//       tokens), converted in registers; P^T is taken straight from the QK
-//       result registers (the D layout of the score MFMA is the B layout of
-//       the PV MFMA).
+// (codes in rows padded to 37 x 16 B, plus the 64 scales).  The page loop
+// takes two pages per step, from two slots, while the next two pages load
+// into the other two.  Wave w owns tokens 16w..16w+15 of every page with its
+// own online softmax state, so no score or maximum crosses waves and a step
+// needs one barrier:
+//   QK  S^T[16 tok x 16 heads] = C . Q^T per page: 18
+//       v_mfma_f32_16x16x32_bf16, the two pages' chains interleaved, the A
+//       fragments read as 8 codes per lane and converted in registers, Q^T
+//       in AGPRs;
+//   PV  O^T[512 x 16 heads] += V^T[512 x 32 tok] . P^T: 32
+//       v_mfma_f32_16x16x32_bf16 over the wave's 16 tokens of both pages,
+//       accumulators in AGPRs; V^T comes from ds_read_b64_tr_b8 (one read
+//       per page gives two 16-column blocks of the wave's tokens), converted
+//       in registers; P^T is taken straight from the QK result registers (the
+//       D layout of the score MFMA, two pages side by side, is the B layout
+//       of the PV MFMA).
 // At the end of a segment the four waves' states are merged through LDS.
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -30,7 +33,6 @@ namespace mla {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -114,83 +116,117 @@ struct State {                     // one wave's running state for its token blo
   float m_ref, l_part;             // reference max (log2 units) of head s; partial row sum
 };
 
-// QK, softmax and PV of one page for wave w's 16 tokens (codes in `slot`).
-__device__ __forceinline__ void page_compute(const LDSP char* __restrict__ codes, const LDSP float* __restrict__ sc,
-                                             const bf16x8 (&qf)[18], int wave, int lane, int nvalid,
-                                             int lo, float s2, State& st) {
+// QK, softmax and PV of two pages a and b of the segment for wave w's 16
+// tokens of each (codes in slots `ca`, `cb`).  A step without a second page
+// passes nvb = 0: every token of b is masked, so its half of every operand is
+// zero whatever its slot holds.  The PV contraction runs over 32
+// tokens per v_mfma_f32_16x16x32_bf16: contraction index 8g + e stands for
+// token 16w + 4g + e of page a when e < 4 and token 16w + 4g + e - 4 of
+// page b when e >= 4, which is where the QK results of lane (g, s) put them.
+__device__ __forceinline__ void pair_compute(const LDSP char* __restrict__ ca, const LDSP char* __restrict__ cb,
+                                             const LDSP float* __restrict__ sca, const LDSP float* __restrict__ scb,
+                                             const bf16x8 (&qf)[18], int wave, int lane, int nva, int loa, int nvb,
+                                             float s2, State& st) {
   const int g = lane >> 4, s = lane & 15;
-  // S^T[tok 16w + 4g + r][head s]; lane (g, s) reads token row 16w + s, codes 32 ks + 8g..+7
-  f32x4 S = {0.f, 0.f, 0.f, 0.f};
+  // S^T[tok 16w + 4g + r][head s] of each page; lane (g, s) reads token row
+  // 16w + s, codes 32 ks + 8g..+7.  The two pages' chains are independent.
+  f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = {0.f, 0.f, 0.f, 0.f};
   {
-    const LDSP char* ap = codes + (16 * wave + s) * kRowF + g * 8;
+    const int ro = (16 * wave + s) * kRowF + g * 8;
+    const LDSP char* ap = ca + ro;
+    const LDSP char* bp = cb + ro;
     constexpr int kPre = 6;
-    i32x2 af[kPre];
+    i32x2 af[kPre], bf[kPre];
 #pragma unroll
-    for (int k = 0; k < kPre; ++k) af[k] = *reinterpret_cast<const LDSP i32x2*>(ap + 32 * k);
+    for (int k = 0; k < kPre; ++k) {
+      af[k] = *reinterpret_cast<const LDSP i32x2*>(ap + 32 * k);
+      bf[k] = *reinterpret_cast<const LDSP i32x2*>(bp + 32 * k);
+    }
 #pragma unroll
     for (int ks = 0; ks < 18; ++ks) {
       const bf16x8 a = cvt8(af[ks % kPre]);
       if (ks + kPre < 18) af[ks % kPre] = *reinterpret_cast<const LDSP i32x2*>(ap + 32 * (ks + kPre));
-      asm volatile("s_nop 1\n v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(S) : "v"(a), "a"(qf[ks]));
+      asm volatile("s_nop 1\n v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(S0) : "v"(a), "a"(qf[ks]));
+      const bf16x8 b = cvt8(bf[ks % kPre]);
+      if (ks + kPre < 18) bf[ks % kPre] = *reinterpret_cast<const LDSP i32x2*>(bp + 32 * (ks + kPre));
+      asm volatile("s_nop 1\n v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+v"(S1) : "v"(b), "a"(qf[ks]));
     }
-    asm volatile("s_nop 7\n s_nop 7\n s_nop 1" ::: "memory");   // MFMA result -> VALU
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 1" ::: "memory");   // MFMA results -> VALU
   }
-  float v[4], scl[4];
+  float v[8], scl[8];
   float mb = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = 16 * wave + 4 * g + r;
-    scl[r] = sc[t];
-    v[r] = (t < nvalid && t >= lo) ? S[r] * s2 * scl[r] : -INFINITY;
-    mb = fmaxf(mb, v[r]);
+    scl[r] = sca[t];
+    v[r] = (t < nva && t >= loa) ? S0[r] * s2 * scl[r] : -INFINITY;
+    scl[4 + r] = scb[t];
+    v[4 + r] = t < nvb ? S1[r] * s2 * scl[4 + r] : -INFINITY;
   }
+#pragma unroll
+  for (int r = 0; r < 8; ++r) mb = fmaxf(mb, v[r]);
   mb = max_xor32(max_xor16(mb));
   float alpha = 1.f;
   if (mb > st.m_ref + kTau) {
     alpha = __builtin_amdgcn_exp2f(st.m_ref - mb);
     st.m_ref = mb;
   }
-  float p[4], ps = 0.f;
+  float p[8], ps = 0.f;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = 16 * wave + 4 * g + r;
-    const bool ok = t < nvalid && t >= lo;
+  for (int r = 0; r < 8; ++r) {
+    const bool ok = v[r] != -INFINITY;
     const float e = ok ? __builtin_amdgcn_exp2f(v[r] - st.m_ref) : 0.f;
     ps += e;
     p[r] = ok ? e * scl[r] : 0.f;
   }
   st.l_part = st.l_part * alpha + ps;
   if (__any(alpha != 1.f)) {
-    asm volatile("s_nop 7\n s_nop 7\n s_nop 1" ::: "memory");  // previous page's MFMAs -> VALU
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 1" ::: "memory");  // previous MFMAs -> VALU
 #pragma unroll
-    for (int cb = 0; cb < 32; ++cb) st.o[cb] *= alpha;
+    for (int c = 0; c < 32; ++c) st.o[c] *= alpha;
   }
-  const u32x2 pk = {pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3])};
-  const s16x4 pf = __builtin_bit_cast(s16x4, pk);
+  const bf16x8 pf = __builtin_bit_cast(
+      bf16x8, u32x4{pack2_bf16(p[0], p[1]), pack2_bf16(p[2], p[3]), pack2_bf16(p[4], p[5]), pack2_bf16(p[6], p[7])});
 
   // V^T: in each 16-lane group g, source lane j names token row 16w + 4g +
   // (j/2 mod 4) and the 8 columns 32 c + 8 (j mod 2) + 16 (j/8); lane s then
   // receives, for tokens 16w + 4g + e, e = 0..3, column 32 c + s (first dword)
-  // and column 32 c + 16 + s (second dword).  Rows outside the window (past
-  // the end of the sequence or before its start) are zeroed after conversion
-  // (their codes may be anything).
+  // and column 32 c + 16 + s (second dword), one read per page.  Rows outside
+  // the window (past the end of the sequence or before its start) are zeroed
+  // after conversion (their codes may be anything).
   const int jj = lane & 15;
-  const LDSP char* vp = codes + (16 * wave + 4 * g + ((jj >> 1) & 3)) * kRowF + 8 * (jj & 1) + 16 * (jj >> 3);
-  auto keep = [&](int t) { return t >= lo && t < nvalid; };
+  const int vo = (16 * wave + 4 * g + ((jj >> 1) & 3)) * kRowF + 8 * (jj & 1) + 16 * (jj >> 3);
+  const LDSP char* vpa = ca + vo;
+  const LDSP char* vpb = cb + vo;
   const int t0 = 16 * wave + 4 * g;
-  const uint32_t keep01 = (keep(t0) ? 0x0000FFFFu : 0u) | (keep(t0 + 1) ? 0xFFFF0000u : 0u);
-  const uint32_t keep23 = (keep(t0 + 2) ? 0x0000FFFFu : 0u) | (keep(t0 + 3) ? 0xFFFF0000u : 0u);
+  auto keep_a = [&](int t) { return t >= loa && t < nva; };
+  auto keep_b = [&](int t) { return t < nvb; };
+  const uint32_t ka01 = (keep_a(t0) ? 0x0000FFFFu : 0u) | (keep_a(t0 + 1) ? 0xFFFF0000u : 0u);
+  const uint32_t ka23 = (keep_a(t0 + 2) ? 0x0000FFFFu : 0u) | (keep_a(t0 + 3) ? 0xFFFF0000u : 0u);
+  const uint32_t kb01 = (keep_b(t0) ? 0x0000FFFFu : 0u) | (keep_b(t0 + 1) ? 0xFFFF0000u : 0u);
+  const uint32_t kb23 = (keep_b(t0 + 2) ? 0x0000FFFFu : 0u) | (keep_b(t0 + 3) ? 0xFFFF0000u : 0u);
   constexpr int kVPre = 4;
-  i32x2 vf[kVPre];
+  i32x2 va[kVPre], vb[kVPre];
 #pragma unroll
-  for (int k = 0; k < kVPre; ++k) vf[k] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vp + 32 * k));
+  for (int k = 0; k < kVPre; ++k) {
+    va[k] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vpa + 32 * k));
+    vb[k] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vpb + 32 * k));
+  }
 #pragma unroll
   for (int c = 0; c < 16; ++c) {
-    const i32x2 w = vf[c % kVPre];
-    if (c + kVPre < 16) vf[c % kVPre] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vp + 32 * (c + kVPre)));
-    const s16x4 a0 = __builtin_bit_cast(s16x4, u32x2{cvt_pair<false>(w[0]) & keep01, cvt_pair<true>(w[0]) & keep23});
-    const s16x4 a1 = __builtin_bit_cast(s16x4, u32x2{cvt_pair<false>(w[1]) & keep01, cvt_pair<true>(w[1]) & keep23});
-    asm volatile("s_nop 1\n v_mfma_f32_16x16x16_bf16 %0, %2, %4, %0\n v_mfma_f32_16x16x16_bf16 %1, %3, %4, %1"
+    const i32x2 wa = va[c % kVPre];
+    const i32x2 wb = vb[c % kVPre];
+    if (c + kVPre < 16) {
+      va[c % kVPre] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vpa + 32 * (c + kVPre)));
+      vb[c % kVPre] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((LDSP i32x2*)(vpb + 32 * (c + kVPre)));
+    }
+    const uint32_t b00 = cvt_pair<false>(wb[0]) & kb01, b01 = cvt_pair<true>(wb[0]) & kb23;
+    const uint32_t b10 = cvt_pair<false>(wb[1]) & kb01, b11 = cvt_pair<true>(wb[1]) & kb23;
+    const bf16x8 a0 =
+        __builtin_bit_cast(bf16x8, u32x4{cvt_pair<false>(wa[0]) & ka01, cvt_pair<true>(wa[0]) & ka23, b00, b01});
+    const bf16x8 a1 =
+        __builtin_bit_cast(bf16x8, u32x4{cvt_pair<false>(wa[1]) & ka01, cvt_pair<true>(wa[1]) & ka23, b10, b11});
+    asm volatile("s_nop 1\n v_mfma_f32_16x16x32_bf16 %0, %2, %4, %0\n v_mfma_f32_16x16x32_bf16 %1, %3, %4, %1"
                  : "+a"(st.o[2 * c]), "+a"(st.o[2 * c + 1]) : "v"(a0), "v"(a1), "v"(pf));
   }
 }
@@ -283,13 +319,23 @@ __global__ void __launch_bounds__(256, 1) decode_fp8_h16(
     st.m_ref = -INFINITY;
     st.l_part = 0.f;
 
-    for (int i = 0; i < n; ++i) {
-      wait_loads(nper * min(2, n - 1 - i));                     // this wave's loads of page i
-      barrier_lds();                                            // everyone's; slot of page i-1 free
-      if (i + 3 < n) issue(i + 3);
-      const int nvalid = (int)min<int64_t>(kBs, (int64_t)L - (jp0 + i) * kBs);
-      page_compute((const LDSP char*)g_ring + (i & 3) * kSlotB, (const LDSP float*)g_sc[i & 3], qf, wave, lane,
-                   nvalid, jp0 + i == 0 ? lo : 0, s2, st);
+    // Two pages per step: pages 2k and 2k+1 are computed from slots (2k) % 4
+    // and (2k+1) % 4 while pages 2k+2 and 2k+3 load into the other two (page 2
+    // went out with the queries; page 3 goes into the query slot once every
+    // wave holds its queries).
+    for (int k = 0; 2 * k < n; ++k) {
+      const int ia = 2 * k, ib = ia + 1;
+      wait_loads(k == 0 && n > 2 ? nper : 0);                   // this wave's loads of pages ia, ib
+      barrier_lds();                                            // everyone's; slots of the previous pair free
+      if (ia + 2 >= 3 && ia + 2 < n) issue(ia + 2);
+      if (ib + 2 < n) issue(ib + 2);
+      const int nva = (int)min<int64_t>(kBs, (int64_t)L - (jp0 + ia) * kBs);
+      const int loa = jp0 + ia == 0 ? lo : 0;
+      const LDSP char* sa = (const LDSP char*)g_ring + (ia & 3) * kSlotB;
+      const LDSP char* sb = (const LDSP char*)g_ring + (ib & 3) * kSlotB;
+      const int nvb = ib < n ? (int)min<int64_t>(kBs, (int64_t)L - (jp0 + ib) * kBs) : 0;
+      pair_compute(sa, sb, (const LDSP float*)g_sc[ia & 3], (const LDSP float*)g_sc[ib & 3], qf, wave, lane,
+                   nva, loa, nvb, s2, st);
     }
 
     // ---- merge the four waves' states, normalise, store ----------------------
