@@ -93,8 +93,14 @@ __global__ void __launch_bounds__(256) kv_proj_finish(int32_t T, int32_t KS, con
     const float* pr = part + ((int64_t)j * T + t) * kRow;
     x0[i] = *reinterpret_cast<const f32x4*>(pr + 8 * lane);
     x1[i] = *reinterpret_cast<const f32x4*>(pr + 8 * lane + 4);
-    y[i] = lane < 32 ? *reinterpret_cast<const f32x2*>(pr + 512 + 2 * lane) : f32x2{0.f, 0.f};
+    // every lane loads (lanes >= 32 re-read pair 31 and drop it), so that no
+    // load sits in a branch whose join would wait for it
+    y[i] = *reinterpret_cast<const f32x2*>(pr + 512 + 2 * min(lane, 31));
   }
+  // the RoPE angle of pair `lane` (float64 sine and cosine) while the partial
+  // sums are in flight
+  double rc = 0.0, rs = 0.0;
+  if (wave == 0 && lane < 32) rope_angle(pos[t], lane, 64, log2_base, &rc, &rs);
   f32x4 c0 = {0.f, 0.f, 0.f, 0.f}, c1 = {0.f, 0.f, 0.f, 0.f};
   f32x2 kr = {0.f, 0.f};
 #pragma unroll
@@ -119,7 +125,7 @@ __global__ void __launch_bounds__(256) kv_proj_finish(int32_t T, int32_t KS, con
   }
   const u32x4_t c = {pack2_bf16(c0[0], c0[1]), pack2_bf16(c0[2], c0[3]), pack2_bf16(c1[0], c1[1]),
                      pack2_bf16(c1[2], c1[3])};
-  append_row_576<kE4M3>(c, pack2_bf16(kr[0], kr[1]), pos[t], slot[t], cache, kv_scale, log2_base, lane);
+  append_row_576_cs<kE4M3>(c, pack2_bf16(kr[0], kr[1]), rc, rs, slot[t], cache, kv_scale, lane);
 }
 
 // Any shape: one workgroup per token, thread o computes output features o,

@@ -92,18 +92,25 @@ template <> struct io<bf16_t> {
 // 2^(-(2i/d_rope) log2(base)) (the caller passes log2(base), computed once on
 // the host); angle, sine, cosine and rotation in float64 without
 // contraction, result rounded to float32.
-__device__ __forceinline__ void rope_pair(float x0, float x1, int32_t pos, int i, int d_rope,
-                                          double log2_base, float* y0, float* y1) {
+__device__ __forceinline__ void rope_angle(int32_t pos, int i, int d_rope, double log2_base, double* c, double* s) {
 #pragma clang fp contract(off)
   const double inv = exp2(-(2.0 * static_cast<double>(i) / static_cast<double>(d_rope)) * log2_base);
   const double ang = static_cast<double>(pos) * inv;
-  double s, c;
-  sincos(ang, &s, &c);
+  sincos(ang, s, c);
+}
+__device__ __forceinline__ void rope_rotate(float x0, float x1, double c, double s, float* y0, float* y1) {
+#pragma clang fp contract(off)
   const double a = static_cast<double>(x0), b = static_cast<double>(x1);
   const double r0 = a * c - b * s;
   const double r1 = a * s + b * c;
   *y0 = static_cast<float>(r0);
   *y1 = static_cast<float>(r1);
+}
+__device__ __forceinline__ void rope_pair(float x0, float x1, int32_t pos, int i, int d_rope,
+                                          double log2_base, float* y0, float* y1) {
+  double c, s;
+  rope_angle(pos, i, d_rope, log2_base, &c, &s);
+  rope_rotate(x0, x1, c, s, y0, y1);
 }
 
 // Workgroup barrier that waits only for this wave's LDS operations.  Direct
@@ -272,20 +279,21 @@ __device__ __forceinline__ float wave_max_all(float x) {
 
 // One 576-wide cache row (d_c = 512, d_R = 64) from bfloat16 inputs, written
 // by one wave: lane l holds latent elements 8l..8l+7 (c, bf16 bits) and, for
-// l < 32, the unrotated RoPE pair l (kp, two bf16).  A bf16 cache receives
+// l < 32, the unrotated RoPE pair l (kp, two bf16) with the cosine and sine
+// of its angle (rc, rs from rope_angle).  A bf16 cache receives
 // the latent bits unchanged (bf16 -> float -> bf16 is exact) and the rotated
 // pair rounded once; an E4M3 cache receives e4m3(x / s) with s = amax / 448
 // over the whole row (1 for an all-zero row), s stored in kv_scale[slot].
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 template <bool kE4M3>
-__device__ __forceinline__ void append_row_576(u32x4_t c, uint32_t kp, int32_t p, int64_t sl, void* cache,
-                                               float* kv_scale, double log2_base, int lane) {
+__device__ __forceinline__ void append_row_576_cs(u32x4_t c, uint32_t kp, double rc, double rs, int64_t sl,
+                                                  void* cache, float* kv_scale, int lane) {
   constexpr int kDc = 512, kDr = 64, kD = 576;
   float y0 = 0.f, y1 = 0.f;
   if (lane < kDr / 2)
-    rope_pair(bf16_to_f32(static_cast<uint16_t>(kp & 0xFFFFu)), bf16_to_f32(static_cast<uint16_t>(kp >> 16)), p, lane,
-              kDr, log2_base, &y0, &y1);
+    rope_rotate(bf16_to_f32(static_cast<uint16_t>(kp & 0xFFFFu)), bf16_to_f32(static_cast<uint16_t>(kp >> 16)), rc, rs,
+                &y0, &y1);
   if constexpr (!kE4M3) {
     uint16_t* dst = static_cast<uint16_t*>(cache) + sl * kD;
     *reinterpret_cast<u32x4_t*>(dst + 8 * lane) = c;
@@ -317,6 +325,15 @@ __device__ __forceinline__ void append_row_576(u32x4_t c, uint32_t kp, int32_t p
           static_cast<uint16_t>(f32_to_e4m3(__fdiv_rn(y0, sc)) | (f32_to_e4m3(__fdiv_rn(y1, sc)) << 8));
     if (lane == 0) kv_scale[sl] = sc;
   }
+}
+
+// The same row with the RoPE angle computed here (lanes < 32, pair = lane).
+template <bool kE4M3>
+__device__ __forceinline__ void append_row_576(u32x4_t c, uint32_t kp, int32_t p, int64_t sl, void* cache,
+                                               float* kv_scale, double log2_base, int lane) {
+  double rc = 0.0, rs = 0.0;
+  if (lane < 32) rope_angle(p, lane, 64, log2_base, &rc, &rs);
+  append_row_576_cs<kE4M3>(c, kp, rc, rs, sl, cache, kv_scale, lane);
 }
 
 // The part of the split-KV schedule one workgroup needs, in two barriers and
