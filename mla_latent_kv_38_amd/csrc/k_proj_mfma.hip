@@ -114,16 +114,14 @@ __global__ void __launch_bounds__(256) absorb_q_mfma(int32_t B, int32_t bpw, int
   int32_t rpos[kRopePer];
 #pragma unroll
   for (int k = 0; k < kRopePer; ++k) {
-    const int i = i_first + k * stride;
-    rx[k][0] = rx[k][1] = 0.f;
-    rpos[k] = 0;
-    if (i < npairs) {
-      const int bb = b_lo + i / half, p = i % half;
-      const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
-      rx[k][0] = bf16_to_f32(q_r[src]);
-      rx[k][1] = bf16_to_f32(q_r[src + 1]);
-      rpos[k] = pos[bb];
-    }
+    // every thread loads (a thread past the last pair re-reads that pair and
+    // drops it), so that no load sits in a branch whose join would wait for it
+    const int i = min(i_first + k * stride, npairs - 1);
+    const int bb = b_lo + i / half, p = i % half;
+    const int64_t src = ((int64_t)bb * n_h + h) * d_R + 2 * p;
+    rx[k][0] = bf16_to_f32(q_r[src]);
+    rx[k][1] = bf16_to_f32(q_r[src + 1]);
+    rpos[k] = pos[bb];
   }
   auto rope_store = [&](int i, float x0, float x1, int32_t ps) {
     const int bb = b_lo + i / half, p = i % half;
